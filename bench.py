@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Float8Linear forward + backward benchmark on one MI355X.
+
+A step is one forward + backward (amax -> scale -> fp8 cast + transposed
+copy -> three fp8 GEMMs with dequantisation) of every linear in the
+workload, through the C ABI (f8lin_forward / f8lin_backward; plus
+f8lin_delayed_update for delayed scaling), on seeded synthetic bf16 inputs
+already resident in HBM.  Prints ONE JSON line.
+
+Timed region: W untimed warm-up steps, synchronize, K timed steps bracketed
+by HIP events on the launch stream, synchronize.  Input sets rotate between
+steps (enough copies that a step's inputs are not left in the 256 MB
+last-level cache by the previous step).
+
+A second, instrumented pass runs the same K steps through the individual
+entry points (amax / cast_transpose / gemm -- the exact launch sequence
+f8lin_forward/backward perform) with HIP events between the calls on the same
+stream, giving each kernel's average duration for the roofline figures.
+
+The oracle (CPU, test infrastructure) is timed on the host cores on a bounded
+sample of the same workload for the cpu_baseline field.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+MALL_BYTES = 256 << 20
+# P3 (pytorch/torchtitan PR #778) single-linear table, (4096, 4096) input,
+# float8nocompile ATOMIC_MAX on H100: 977.858 (read as microseconds) for
+# forward + backward of a 4096->4096 linear -> 6*4096^3 / 977.858 us.
+H100_BASELINE_TFLOPS = {"linear4096_m4096": 6 * 4096 ** 3 / 977.858e-6 / 1e12,
+                        "linear4096_m16": 6 * 16 * 4096 ** 2 / 386.469e-6 / 1e12,
+                        "linear4096_m256": 6 * 256 * 4096 ** 2 / 408.137e-6 / 1e12,
+                        "linear4096_m65536_outliers": 6 * 65536 * 4096 ** 2 / 10813.3e-6 / 1e12}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="linear4096_m4096")
+    p.add_argument("--algo", default="atomic", choices=["atomic", "twopass"])
+    p.add_argument("--rotate", type=int, default=0, help="input sets to rotate (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="rows of X/dY in the oracle's timed sample")
+    p.add_argument("--only-timed", action="store_true", help="skip the instrumented pass (for profiling)")
+    return p.parse_args()
+
+
+def sha256_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(gemm_src):
+    """HBM traffic of the GEMM from rocprofv3 counter runs, if the committed
+    record was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha256_of(gemm_src):
+        return None
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   f"(got {args.gpus}); multi-GPU sharding is design-only"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from float8linear_tensorwise_amax_amd import f8lin, inputs
+
+    wl = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    delayed = wl.scaling == "delayed"
+
+    # ---- inputs: R rotating sets, generated on the host, copied once to HBM
+    per_set_bytes = sum(2 * (l.M * l.K + l.N * l.K + l.M * l.N) for l in wl.linears)
+    R = args.rotate or max(1, min(8, math.ceil(3 * MALL_BYTES / per_set_bytes)))
+    sets = []
+    for r in range(R):
+        step_in = inputs.workload_inputs(wl, r if delayed else 0)
+        if r > 0 and not delayed:  # distinct data per set: reseed
+            gen = torch.Generator().manual_seed(1000 + r)
+            step_in = [(l, *inputs.draw_linear(gen, l, wl.outlier_fraction, wl.outlier_multiplier))
+                       for l in wl.linears]
+        sets.append([(l, x.to(dev), w.to(dev), dy.to(dev)) for (l, x, w, dy) in step_in])
+    bufs = [f8lin.LinearBuffers(l.M, l.N, l.K, dev) for l in wl.linears]
+    torch.cuda.synchronize()
+
+    def step(t):
+        mode = "delayed" if (delayed and t > 0) else "dynamic"
+        for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
+            buf.forward(x, w, mode, args.algo)
+            buf.backward(dy, mode, args.algo)
+            if delayed:
+                f8lin.delayed_update(buf.states())
+
+    # ---- timed region
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_host0 = time.perf_counter()
+    e0.record(stream)
+    for t in range(args.steps):
+        step(args.warmup + t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    flops = wl.flops
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    out = {
+        "metric": "Float8Linear fwd+bwd us & TFLOP/s (frac fp8 peak); cast/amax HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(tflops / H100_BASELINE_TFLOPS[args.workload], 3)
+                        if args.workload in H100_BASELINE_TFLOPS else None),
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "linears": [{"name": l.name, "M": l.M, "K": l.K, "N": l.N} for l in wl.linears],
+                   "scaling": wl.scaling, "amax_algo": args.algo, "rotating_input_sets": R,
+                   "inputs": "X~N(0,1), W~N(0,1/K), dY~N(0,1e-3) bf16, seeded"},
+        "fwd_bwd_us": round(ms_per_step * 1e3, 2),
+        "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "host_wall_s_timed": round(t_host, 4),
+    }
+    if out["vs_baseline"] is not None:
+        out["baseline_note"] = ("pages' H100 float8nocompile ATOMIC_MAX fwd+bwd time for this shape "
+                                "(read as microseconds), converted to TFLOP/s; another machine's number")
+
+    if not args.only_timed:
+        out.update(instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed))
+        rl = out["kernels"]["gemm"]
+        traffic = load_traffic(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "csrc", "gemm.hip"))
+        out["roofline"] = {"kernel": "gemm_fp8_tn", "bound": "mfma", "achieved": rl["tflops"],
+                           "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(rl["tflops"] / PEAK_FP8_TFLOPS, 4),
+                           "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None)}
+        if traffic:
+            out["roofline"]["traffic_note"] = traffic.get("note", "")
+            out["roofline"]["algorithmic_bytes_per_launch"] = rl["algorithmic_bytes_per_launch"]
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, wl, sets, np, torch)
+    print(json.dumps(out), flush=True)
+
+
+def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
+    """Per-kernel durations: the same launch sequence as f8lin_forward /
+    f8lin_backward, issued entry point by entry point with HIP events between
+    the calls on the launch stream."""
+    acc = {"amax": [0.0, 0, 0.0], "cast": [0.0, 0, 0.0], "gemm": [0.0, 0, 0.0]}  # ms, launches, units
+    gemm_bytes = []
+
+    def timed(kind, fn, units):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        pending.append((kind, a, b, units))
+
+    for t in range(args.warmup + args.steps):
+        pending = []
+        mode = "delayed" if (delayed and t > 0) else "dynamic"
+        for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
+            if mode == "dynamic":
+                timed("amax", lambda: f8lin.amax(x, buf.sx.amax, buf.ws, args.algo), x.numel())
+                timed("amax", lambda: f8lin.amax(w, buf.sw.amax, buf.ws, args.algo), w.numel())
+            timed("cast", lambda: f8lin.cast_transpose(x, "e4m3", mode, buf.sx, buf.x8, buf.x8t), x.numel())
+            timed("cast", lambda: f8lin.cast_transpose(w, "e4m3", mode, buf.sw, buf.w8, buf.w8t), w.numel())
+            timed("gemm", lambda: f8lin.gemm(buf.x8, "e4m3", buf.w8, "e4m3", buf.sx.inv_scale, buf.sw.inv_scale,
+                                             buf.y), 2 * l.M * l.N * l.K)
+            if mode == "dynamic":
+                timed("amax", lambda: f8lin.amax(dy, buf.sdy.amax, buf.ws, args.algo), dy.numel())
+            timed("cast", lambda: f8lin.cast_transpose(dy, "e5m2", mode, buf.sdy, buf.dy8, buf.dy8t), dy.numel())
+            timed("gemm", lambda: f8lin.gemm(buf.dy8, "e5m2", buf.w8t, "e4m3", buf.sdy.inv_scale, buf.sw.inv_scale,
+                                             buf.dx), 2 * l.M * l.N * l.K)
+            timed("gemm", lambda: f8lin.gemm(buf.dy8t, "e5m2", buf.x8t, "e4m3", buf.sdy.inv_scale,
+                                             buf.sx.inv_scale, buf.dw), 2 * l.M * l.N * l.K)
+            if delayed:
+                f8lin.delayed_update(buf.states())
+            if t == 0:
+                gemm_bytes.extend([l.M * l.K + l.N * l.K + 2 * l.M * l.N, l.M * l.N + l.N * l.K + 2 * l.M * l.K,
+                                   l.M * l.N + l.M * l.K + 2 * l.N * l.K])
+        torch.cuda.synchronize()
+        if t >= args.warmup:
+            for kind, a, b, units in pending:
+                acc[kind][0] += a.elapsed_time(b)
+                acc[kind][1] += 1
+                acc[kind][2] += units
+    k = {}
+    ms, n, el = acc["gemm"]
+    k["gemm"] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
+                 "tflops": round(el / (ms * 1e-3) / 1e12, 2),
+                 "algorithmic_bytes_per_launch": int(sum(gemm_bytes) / len(gemm_bytes)),
+                 "flops_per_launch": int(el / n)}
+    ms, n, el = acc["cast"]
+    k["cast_transpose"] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
+                           "gbs": round(4 * el / (ms * 1e-3) / 1e9, 1),
+                           "frac_hbm_peak": round(4 * el / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "bytes_per_elem": 4}
+    ms, n, el = acc["amax"]
+    if n:
+        k["amax_" + args.algo] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
+                                  "gbs": round(2 * el / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(2 * el / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                  "bytes_per_elem": 2}
+    return {"kernels": k}
+
+
+def cpu_baseline(args, wl, sets, np, torch):
+    """The oracle (as it stands) on a bounded sample of the workload: the first
+    `cpu_rows` rows of X and dY of each linear with the full W -- amax, scale,
+    cast + transpose of all three tensors and the three fp64 GEMM references."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    flops = 0
+    secs = 0.0
+    rows_used = []
+    for (l, x, w, dy) in sets[0]:
+        ms = min(l.M, args.cpu_rows)
+        rows_used.append(ms)
+        xb, wb, dyb = bits(x[:ms]), bits(w), bits(dy[:ms])
+        t0 = time.perf_counter()
+        oracle.linear_step(xb, wb, dyb, gemms=True)
+        secs += time.perf_counter() - t0
+        flops += 6 * ms * l.N * l.K
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(secs, 2),
+            "sample": f"one step of {wl.name} on the first {rows_used} rows of X and dY per linear (full W): "
+                      "amax, scale, cast+transpose of X, W, dY and the three fp64 GEMM references",
+            "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+// Tensorwise amax of a bf16 tensor, two algorithms (the ATOMIC_MAX and
+// REDUCTION kernel_algo rows of the single-linear-layer table in
+// pytorch/torchtitan PR #778):
+//   atomic : one launch; each workgroup reduces its grid-stride share and folds
+//            it into one device-wide slot with an atomic max; the last
+//            workgroup to finish (ticket counter) publishes the result and
+//            clears the slot and ticket for the next call.
+//   twopass: the same per-workgroup reduction writes one partial per
+//            workgroup; a second launch of one workgroup reduces them.
+// Both compute max |x| exactly as the max of the 15-bit magnitude fields, so
+// both give the same bits as a plain max over |x| in any order.
+//
+// HBM-bound: 2 bytes read per element.  Loads are 128-bit (8 bf16), four in
+// flight per thread per iteration; the grid is capped at kAmaxMaxBlocks
+// workgroups that stride over the tensor.  Loads are ordinary (cached): the
+// cast that follows re-reads the same tensor and can hit in the last-level
+// cache when the tensor fits.
+#include "device_common.h"
+#include "internal.h"
+
+namespace f8lin {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+// Max magnitude (15-bit) over this thread's grid-stride share of x[0, n).
+__device__ __forceinline__ uint32_t thread_magmax(const uint16_t *__restrict__ x, int64_t n, int64_t gtid,
+                                                  int64_t nthreads) {
+  const u32x4 *__restrict__ xv = reinterpret_cast<const u32x4 *>(x);
+  const int64_t nv = n >> 3;  // whole 8-element vectors
+  uint32_t m = 0;
+  int64_t i = gtid;
+  for (; i + (kUnroll - 1) * nthreads < nv; i += kUnroll * nthreads) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = xv[i + u * nthreads];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      m = mag_max2(m, v[u].x);
+      m = mag_max2(m, v[u].y);
+      m = mag_max2(m, v[u].z);
+      m = mag_max2(m, v[u].w);
+    }
+  }
+  for (; i < nv; i += nthreads) {
+    const u32x4 v = xv[i];
+    m = mag_max2(m, v.x);
+    m = mag_max2(m, v.y);
+    m = mag_max2(m, v.z);
+    m = mag_max2(m, v.w);
+  }
+  const int64_t tail = n - (nv << 3);  // < 8 trailing elements
+  if (gtid < tail) m = max(m, (uint32_t)x[(nv << 3) + gtid] & 0x7FFFu);
+  return m;
+}
+
+// Workgroup max; the result is valid in thread 0.
+__device__ __forceinline__ uint32_t block_max(uint32_t v) {
+  __shared__ uint32_t red[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) v = max(v, red[w]);
+    v = max(v, red[0]);
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_atomic_kernel(const uint16_t *__restrict__ x, int64_t n,
+                                                               uint32_t *ws, float *amax_out) {
+  const int64_t nthreads = (int64_t)gridDim.x * kThreads;
+  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t m = block_max(thread_magmax(x, n, gtid, nthreads));
+  if (threadIdx.x == 0) {
+    atomicMax(&ws[0], m);
+    __threadfence();
+    const uint32_t ticket = atomicAdd(&ws[1], 1u);
+    if (ticket == gridDim.x - 1) {  // every other workgroup has folded its max in
+      __threadfence();
+      const uint32_t all = atomicMax(&ws[0], 0u);  // atomic read of the final max
+      amax_out[0] = __uint_as_float(all << 16);
+      atomicExch(&ws[0], 0u);
+      atomicExch(&ws[1], 0u);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t *__restrict__ x, int64_t n,
+                                                                uint32_t *__restrict__ partials) {
+  const int64_t nthreads = (int64_t)gridDim.x * kThreads;
+  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t m = block_max(thread_magmax(x, n, gtid, nthreads));
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Reduces the partials and clears them, so the workspace is zero again.
+__global__ __launch_bounds__(kThreads) void amax_final_kernel(uint32_t *__restrict__ partials, int nparts,
+                                                              float *amax_out) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) {
+    m = max(m, partials[i]);
+    partials[i] = 0u;
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) amax_out[0] = __uint_as_float(m << 16);
+}
+
+int grid_for(int64_t n) {
+  const int64_t nv = n >> 3;
+  const int64_t per_block = (int64_t)kThreads * kUnroll;
+  int64_t g = (nv + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > kAmaxMaxBlocks) g = kAmaxMaxBlocks;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, uint32_t *ws,
+                       hipStream_t stream) {
+  const int grid = grid_for(n);
+  if (algo == F8LIN_AMAX_ATOMIC) {
+    amax_atomic_kernel<<<grid, kThreads, 0, stream>>>(x, n, ws, amax_out);
+  } else {
+    uint32_t *partials = ws + kWsPartialsOffset;
+    amax_partial_kernel<<<grid, kThreads, 0, stream>>>(x, n, partials);
+    amax_final_kernel<<<1, kThreads, 0, stream>>>(partials, grid, amax_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace f8lin

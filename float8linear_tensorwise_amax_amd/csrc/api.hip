@@ -1,0 +1,284 @@
+// C ABI of libf8lin (declared in include/f8lin.h): argument validation, then
+// the launch sequence of each entry point on the caller's stream.  Nothing
+// here synchronises, reads device memory, or allocates.
+//
+// Forward / backward orchestration follows the layer's definition:
+//   forward : [amax X] [amax W] cast X -> X8, X8^T; cast W -> W8, W8^T;
+//             Y = X8 . W8^T / (s_x s_w)
+//   backward: [amax dY] cast dY -> dY8, dY8^T (e5m2);
+//             dX = dY8 . (W8^T)^T / (s_dy s_w); dW = dY8^T . (X8^T)^T / (s_dy s_x)
+// (amax passes only for tensors in dynamic mode; in delayed mode the cast
+// takes its scale from the history and accumulates this step's amax.)
+// The delayed-scaling history update runs after backward, as the sync call
+// after loss.backward() does in pytorch/ao issue #1297's repro script.
+#include <stdint.h>
+#include <string.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace f8lin {
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;        // per matrix dimension
+constexpr int64_t kMaxElems = (int64_t)1 << 40;      // per tensor
+constexpr int kUpdateBatch = 16;
+
+struct StateBatch {
+  f8lin_state s[kUpdateBatch];
+  int n;
+};
+
+__global__ void delayed_update_kernel(StateBatch batch) {
+  const int i = threadIdx.x;
+  if (i >= batch.n) return;
+  const f8lin_state st = batch.s[i];
+  int32_t count = st.hist_meta[0];
+  int32_t pos = st.hist_meta[1];
+  pos = ((pos % kHistLen) + kHistLen) % kHistLen;
+  st.history[pos] = st.amax[0];
+  st.hist_meta[1] = (pos + 1) % kHistLen;
+  st.hist_meta[0] = count < kHistLen ? count + 1 : kHistLen;
+  st.amax[0] = 0.0f;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A data pointer may be NULL only when its tensor is empty.
+bool missing(const void *p, int64_t elems) { return p == nullptr && elems > 0; }
+
+bool bad_dim(int64_t d) { return d < 0 || d > kMaxDim || (d % 16) != 0; }
+
+struct Range {
+  const void *p;
+  int64_t bytes;
+};
+
+bool overlaps(const Range &a, const Range &b) {
+  if (a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + (uintptr_t)a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + (uintptr_t)b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output range must be disjoint from every other range.
+bool any_overlap(const Range *outs, int nout, const Range *ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+int check_fmt(int f) { return (f == F8LIN_E4M3 || f == F8LIN_E5M2) ? F8LIN_OK : F8LIN_EINVAL; }
+int check_algo(int a) { return (a == F8LIN_AMAX_ATOMIC || a == F8LIN_AMAX_TWOPASS) ? F8LIN_OK : F8LIN_EINVAL; }
+int check_mode(int m) { return (m == F8LIN_DYNAMIC || m == F8LIN_DELAYED) ? F8LIN_OK : F8LIN_EINVAL; }
+
+int check_state(const f8lin_state &st, int mode) {
+  if (!st.amax || !st.scale) return F8LIN_EINVAL;
+  if (mode == F8LIN_DELAYED && (!st.history || !st.hist_meta)) return F8LIN_EINVAL;
+  return F8LIN_OK;
+}
+
+int check_ws(const void *ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < kWorkspaceBytes || !aligned16(ws)) return F8LIN_EWORKSPACE;
+  return F8LIN_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? F8LIN_OK : F8LIN_EHIP; }
+
+#define F8_TRY(expr)                 \
+  do {                               \
+    const int st_ = (expr);          \
+    if (st_ != F8LIN_OK) return st_; \
+  } while (0)
+
+// Validation shared by f8lin_cast_transpose and the orchestrated casts.
+int validate_cast(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode, const f8lin_state *st,
+                  const uint8_t *q, const uint8_t *qt) {
+  if (!st) return F8LIN_EINVAL;
+  F8_TRY(check_fmt(fmt));
+  F8_TRY(check_mode(mode));
+  F8_TRY(check_state(*st, mode));
+  if (bad_dim(rows) || bad_dim(cols) || rows * cols > kMaxElems) return F8LIN_ESHAPE;
+  if (missing(x, rows * cols) || missing(q, rows * cols)) return F8LIN_EINVAL;
+  if (!aligned16(x) || !aligned16(q) || (qt && !aligned16(qt))) return F8LIN_EALIGN;
+  const int64_t n = rows * cols;
+  const Range outs[3] = {{q, n}, {qt, qt ? n : 0}, {st->scale, 8}};
+  const Range ins[3] = {{x, 2 * n}, {st->amax, 4}, {st->history, mode == F8LIN_DELAYED ? 64 : 0}};
+  if (any_overlap(outs, 3, ins, 3)) return F8LIN_EINVAL;
+  return F8LIN_OK;
+}
+
+int validate_gemm(const uint8_t *a, int fa, const uint8_t *b, int fb, int64_t M, int64_t N, int64_t K,
+                  const float *ia, const float *ib, const uint16_t *c) {
+  if (!ia || !ib) return F8LIN_EINVAL;
+  F8_TRY(check_fmt(fa));
+  F8_TRY(check_fmt(fb));
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K) || M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems)
+    return F8LIN_ESHAPE;
+  if (missing(a, M * K) || missing(b, N * K) || missing(c, M * N)) return F8LIN_EINVAL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return F8LIN_EALIGN;
+  const Range outs[1] = {{c, 2 * M * N}};
+  const Range ins[4] = {{a, M * K}, {b, N * K}, {ia, 4}, {ib, 4}};
+  if (any_overlap(outs, 1, ins, 4)) return F8LIN_EINVAL;
+  return F8LIN_OK;
+}
+
+}  // namespace
+}  // namespace f8lin
+
+using namespace f8lin;
+
+extern "C" {
+
+size_t f8lin_workspace_bytes(void) { return kWorkspaceBytes; }
+
+const char *f8lin_status_str(int status) {
+  switch (status) {
+    case F8LIN_OK: return "F8LIN_OK";
+    case F8LIN_EINVAL: return "F8LIN_EINVAL: invalid argument (null pointer, enum, overlap or count)";
+    case F8LIN_ESHAPE: return "F8LIN_ESHAPE: dimension negative, too large, or not a multiple of 16";
+    case F8LIN_EALIGN: return "F8LIN_EALIGN: pointer not 16-byte aligned";
+    case F8LIN_EWORKSPACE: return "F8LIN_EWORKSPACE: workspace missing, misaligned or too small";
+    case F8LIN_EHIP: return "F8LIN_EHIP: HIP launch failed";
+    default: return "unknown f8lin status";
+  }
+}
+
+int f8lin_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, void *ws, size_t ws_bytes,
+               void *stream) {
+  if (!amax_out) return F8LIN_EINVAL;
+  F8_TRY(check_algo(algo));
+  if (n < 0 || n > kMaxElems) return F8LIN_ESHAPE;
+  if (missing(x, n)) return F8LIN_EINVAL;
+  if (!aligned16(x)) return F8LIN_EALIGN;
+  F8_TRY(check_ws(ws, ws_bytes));
+  const Range outs[2] = {{amax_out, 4}, {ws, (int64_t)kWorkspaceBytes}};
+  const Range ins[1] = {{x, 2 * n}};
+  if (any_overlap(outs, 2, ins, 1)) return F8LIN_EINVAL;
+  return status_of(launch_amax(x, n, algo, amax_out, (uint32_t *)ws, (hipStream_t)stream));
+}
+
+int f8lin_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
+                         const f8lin_state *st, uint8_t *q, uint8_t *qt, void *stream) {
+  F8_TRY(validate_cast(x, rows, cols, fmt, mode, st, q, qt));
+  return status_of(launch_cast_transpose(x, rows, cols, fmt, mode, *st, q, qt, (hipStream_t)stream));
+}
+
+int f8lin_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, void *stream) {
+  F8_TRY(check_fmt(fmt));
+  if (n < 0 || n > kMaxElems) return F8LIN_ESHAPE;
+  if (missing(v, n) || missing(q, n)) return F8LIN_EINVAL;
+  if (!aligned16(v) || !aligned16(q)) return F8LIN_EALIGN;
+  const Range outs[1] = {{q, n}};
+  const Range ins[1] = {{v, 4 * n}};
+  if (any_overlap(outs, 1, ins, 1)) return F8LIN_EINVAL;
+  return status_of(launch_cast_f32(v, n, fmt, q, (hipStream_t)stream));
+}
+
+int f8lin_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t M, int64_t N, int64_t K,
+               const float *inv_scale_a, const float *inv_scale_b, uint16_t *c, void *stream) {
+  F8_TRY(validate_gemm(a, fmt_a, b, fmt_b, M, N, K, inv_scale_a, inv_scale_b, c));
+  return status_of(launch_gemm(a, fmt_a, b, fmt_b, M, N, K, inv_scale_a, inv_scale_b, c, (hipStream_t)stream));
+}
+
+int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
+  if (!p) return F8LIN_EINVAL;
+  const f8lin_fwd_args a = *p;
+  F8_TRY(check_mode(a.mode_x));
+  F8_TRY(check_mode(a.mode_w));
+  F8_TRY(check_algo(a.algo));
+  F8_TRY(check_state(a.sx, a.mode_x));
+  F8_TRY(check_state(a.sw, a.mode_w));
+  if (bad_dim(a.M) || bad_dim(a.N) || bad_dim(a.K) || a.M * a.K > kMaxElems || a.N * a.K > kMaxElems ||
+      a.M * a.N > kMaxElems)
+    return F8LIN_ESHAPE;
+  if (missing(a.x, a.M * a.K) || missing(a.x8, a.M * a.K) || missing(a.x8t, a.M * a.K) ||
+      missing(a.w, a.N * a.K) || missing(a.w8, a.N * a.K) || missing(a.w8t, a.N * a.K) || missing(a.y, a.M * a.N))
+    return F8LIN_EINVAL;
+  if (!aligned16(a.x) || !aligned16(a.w) || !aligned16(a.y) || !aligned16(a.x8) || !aligned16(a.x8t) ||
+      !aligned16(a.w8) || !aligned16(a.w8t))
+    return F8LIN_EALIGN;
+  const bool need_ws = a.mode_x == F8LIN_DYNAMIC || a.mode_w == F8LIN_DYNAMIC;
+  if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
+  const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
+  const Range outs[10] = {{a.y, 2 * mn},   {a.x8, mk},   {a.x8t, mk},
+                          {a.w8, nk},      {a.w8t, nk},  {a.sx.scale, 8},
+                          {a.sw.scale, 8}, {a.sx.amax, 4}, {a.sw.amax, 4},
+                          {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0}};
+  const Range ins[4] = {{a.x, 2 * mk}, {a.w, 2 * nk}, {a.sx.history, a.mode_x == F8LIN_DELAYED ? 64 : 0},
+                        {a.sw.history, a.mode_w == F8LIN_DELAYED ? 64 : 0}};
+  if (any_overlap(outs, 10, ins, 4)) return F8LIN_EINVAL;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *ws = (uint32_t *)a.ws;
+  if (a.mode_x == F8LIN_DYNAMIC) F8_TRY(status_of(launch_amax(a.x, mk, a.algo, a.sx.amax, ws, s)));
+  if (a.mode_w == F8LIN_DYNAMIC) F8_TRY(status_of(launch_amax(a.w, nk, a.algo, a.sw.amax, ws, s)));
+  F8_TRY(status_of(launch_cast_transpose(a.x, a.M, a.K, F8LIN_E4M3, a.mode_x, a.sx, a.x8, a.x8t, s)));
+  F8_TRY(status_of(launch_cast_transpose(a.w, a.N, a.K, F8LIN_E4M3, a.mode_w, a.sw, a.w8, a.w8t, s)));
+  return status_of(
+      launch_gemm(a.x8, F8LIN_E4M3, a.w8, F8LIN_E4M3, a.M, a.N, a.K, a.sx.scale + 1, a.sw.scale + 1, a.y, s));
+}
+
+int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
+  if (!p) return F8LIN_EINVAL;
+  const f8lin_bwd_args a = *p;
+  if (!a.sx.scale || !a.sw.scale) return F8LIN_EINVAL;
+  F8_TRY(check_mode(a.mode_dy));
+  F8_TRY(check_algo(a.algo));
+  F8_TRY(check_state(a.sdy, a.mode_dy));
+  if (bad_dim(a.M) || bad_dim(a.N) || bad_dim(a.K) || a.M * a.K > kMaxElems || a.N * a.K > kMaxElems ||
+      a.M * a.N > kMaxElems)
+    return F8LIN_ESHAPE;
+  if (missing(a.dy, a.M * a.N) || missing(a.dy8, a.M * a.N) || missing(a.dy8t, a.M * a.N) ||
+      missing(a.x8t, a.M * a.K) || missing(a.dx, a.M * a.K) || missing(a.w8t, a.N * a.K) ||
+      missing(a.dw, a.N * a.K))
+    return F8LIN_EINVAL;
+  if (!aligned16(a.dy) || !aligned16(a.x8t) || !aligned16(a.w8t) || !aligned16(a.dx) || !aligned16(a.dw) ||
+      !aligned16(a.dy8) || !aligned16(a.dy8t))
+    return F8LIN_EALIGN;
+  const bool need_ws = a.mode_dy == F8LIN_DYNAMIC;
+  if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
+  const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
+  const Range outs[7] = {{a.dx, 2 * mk},     {a.dw, 2 * nk},   {a.dy8, mn}, {a.dy8t, mn},
+                         {a.sdy.scale, 8}, {a.sdy.amax, 4}, {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0}};
+  const Range ins[6] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
+                        {a.sx.scale, 8}, {a.sw.scale, 8}, {a.sdy.history, a.mode_dy == F8LIN_DELAYED ? 64 : 0}};
+  if (any_overlap(outs, 7, ins, 6)) return F8LIN_EINVAL;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *ws = (uint32_t *)a.ws;
+  if (a.mode_dy == F8LIN_DYNAMIC) F8_TRY(status_of(launch_amax(a.dy, mn, a.algo, a.sdy.amax, ws, s)));
+  F8_TRY(status_of(launch_cast_transpose(a.dy, a.M, a.N, F8LIN_E5M2, a.mode_dy, a.sdy, a.dy8, a.dy8t, s)));
+  // dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N.
+  F8_TRY(status_of(launch_gemm(a.dy8, F8LIN_E5M2, a.w8t, F8LIN_E4M3, a.M, a.K, a.N, a.sdy.scale + 1,
+                               a.sw.scale + 1, a.dx, s)));
+  // dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
+  return status_of(launch_gemm(a.dy8t, F8LIN_E5M2, a.x8t, F8LIN_E4M3, a.N, a.K, a.M, a.sdy.scale + 1,
+                               a.sx.scale + 1, a.dw, s));
+}
+
+int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream) {
+  if (!states || n_states < 0) return F8LIN_EINVAL;
+  for (int i = 0; i < n_states; ++i) {
+    const f8lin_state &st = states[i];
+    if (!st.amax || !st.history || !st.hist_meta) return F8LIN_EINVAL;
+    if (!aligned16(st.history)) return F8LIN_EALIGN;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int i0 = 0; i0 < n_states; i0 += kUpdateBatch) {
+    StateBatch b;
+    memset(&b, 0, sizeof b);
+    b.n = n_states - i0 < kUpdateBatch ? n_states - i0 : kUpdateBatch;
+    for (int i = 0; i < b.n; ++i) b.s[i] = states[i0 + i];
+    delayed_update_kernel<<<1, 64, 0, s>>>(b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return F8LIN_EHIP;
+  }
+  return F8LIN_OK;
+}
+
+}  // extern "C"

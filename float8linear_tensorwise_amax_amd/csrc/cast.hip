@@ -1,0 +1,228 @@
+// Scale + saturating fp8 cast of a bf16 (rows, cols) tensor, writing the
+// row-major codes q and the transposed codes qt in one pass (the backward
+// GEMMs contract over the other dimension and read qt).
+//
+// Tensorwise scaling (pytorch/torchtitan PR #778 Summary: tensorwise dynamic
+// scaling; pytorch/ao issue #1297 repro: delayed scaling of input, weight and
+// grad_output).  The scale is computed in every workgroup's prologue from the
+// state (dynamic: state.amax; delayed: max of the 16-entry amax history), so
+// no extra launch and no host round trip sit between amax and cast.
+//
+// Work decomposition (gfx950, wave64): one workgroup of 256 threads per
+// 128 x 128 tile.
+//   load   : thread t reads 16 consecutive bf16 (two 128-bit loads) of rows
+//            t/8 + 32p, p = 0..3; eight threads cover one 256-byte row segment.
+//   q      : the 16 codes go out as one 128-bit store (a 128-byte row segment
+//            per 8 threads) and into LDS.
+//   qt     : thread (k = t%8, g = t/8) reads the 4-byte column group g of the
+//            16 tile rows 16k..16k+15 from LDS, transposes the four 4x4 byte
+//            blocks in registers (v_perm_b32), and writes four 128-bit qt
+//            stores; eight neighbouring threads fill one 128-byte qt segment.
+//   LDS    : 128 rows x 128 bytes, 16-byte chunks XOR-swizzled by
+//            (row / 16) % 8, which makes both the 128-bit row writes and the
+//            4-byte column reads spread over all banks.
+// Delayed mode also folds max |x| of the tile into state.amax (atomic max on
+// the fp32 bit pattern, which orders like the value for non-negative floats).
+//
+// HBM-bound: 2 bytes read + 2 bytes written per element (4 B/elem).
+#include "device_common.h"
+#include "internal.h"
+
+namespace f8lin {
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int lds_word(int row, int word) {
+  // 32 words per row; 16-byte chunk index XOR (row / 16) % 8.
+  return row * 32 + ((((word >> 2) ^ (row >> 4)) & 7) << 2) + (word & 3);
+}
+
+// Transposes a 4x4 byte block: d[r] holds bytes (r, 0..3); returns e[c]
+// holding bytes (0..3, c).
+__device__ __forceinline__ void transpose4x4(const uint32_t d0, const uint32_t d1, const uint32_t d2,
+                                             const uint32_t d3, uint32_t &e0, uint32_t &e1, uint32_t &e2,
+                                             uint32_t &e3) {
+  // v_perm_b32(hi, lo, sel): selector byte 0-3 picks lo's bytes, 4-7 hi's.
+  const uint32_t t0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.0 d1.0 d0.1 d1.1
+  const uint32_t t1 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.2 d1.2 d0.3 d1.3
+  const uint32_t t2 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);  // d2.0 d3.0 d2.1 d3.1
+  const uint32_t t3 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);  // d2.2 d3.2 d2.3 d3.3
+  e0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);                 // d0.0 d1.0 d2.0 d3.0
+  e1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);                 // d0.1 d1.1 d2.1 d3.1
+  e2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);                 // d0.2 d1.2 d2.2 d3.2
+  e3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);                 // d0.3 d1.3 d2.3 d3.3
+}
+
+template <int FMT, int MODE, bool WRITE_T>
+__global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ amax_in,
+    const float *__restrict__ history, float *amax_acc, float *scale_out, uint8_t *__restrict__ q,
+    uint8_t *__restrict__ qt, int tiles_x) {
+  __shared__ uint32_t tile[kTile * kTile / 4];
+  __shared__ uint32_t red[kThreads / 64];
+  constexpr float fm = fmt_max<FMT>();
+
+  float a;
+  if constexpr (MODE == F8LIN_DYNAMIC) {
+    a = amax_in[0];
+  } else {
+    a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kHistLen; ++i) {
+      const float h = history[i];
+      a = (h != h || a != a) ? __builtin_nanf("") : fmaxf(a, h);
+    }
+  }
+  const float s = scale_from_amax(a, fm);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    scale_out[0] = s;
+    scale_out[1] = 1.0f / s;
+  }
+
+  const int t = threadIdx.x;
+  const int64_t row0 = (int64_t)(blockIdx.x / tiles_x) * kTile;
+  const int64_t col0 = (int64_t)(blockIdx.x % tiles_x) * kTile;
+  const int c16 = t & 7;
+  const int rsub = t >> 3;
+  const int64_t gcol = col0 + c16 * 16;
+  const bool col_ok = gcol < cols;
+
+  u32x4 in[4][2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t grow = row0 + rsub + 32 * p;
+    if (col_ok && grow < rows) {
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(x + grow * cols + gcol);
+      in[p][0] = src[0];
+      in[p][1] = src[1];
+    } else {
+      in[p][0] = u32x4{0, 0, 0, 0};
+      in[p][1] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  uint32_t mag = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = rsub + 32 * p;
+    const int64_t grow = row0 + r;
+    u32x4 o;
+    o.x = quantize4<FMT>(in[p][0].x, in[p][0].y, s);
+    o.y = quantize4<FMT>(in[p][0].z, in[p][0].w, s);
+    o.z = quantize4<FMT>(in[p][1].x, in[p][1].y, s);
+    o.w = quantize4<FMT>(in[p][1].z, in[p][1].w, s);
+    if constexpr (MODE == F8LIN_DELAYED) {
+      mag = mag_max2(mag, in[p][0].x);
+      mag = mag_max2(mag, in[p][0].y);
+      mag = mag_max2(mag, in[p][0].z);
+      mag = mag_max2(mag, in[p][0].w);
+      mag = mag_max2(mag, in[p][1].x);
+      mag = mag_max2(mag, in[p][1].y);
+      mag = mag_max2(mag, in[p][1].z);
+      mag = mag_max2(mag, in[p][1].w);
+    }
+    if (col_ok && grow < rows) *reinterpret_cast<u32x4 *>(q + grow * cols + gcol) = o;
+    if constexpr (WRITE_T) *reinterpret_cast<u32x4 *>(&tile[lds_word(r, c16 * 4)]) = o;
+  }
+
+  if constexpr (MODE == F8LIN_DELAYED) {
+    // Out-of-range elements were loaded as +0 and cannot raise the max.
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = mag;
+  }
+
+  if constexpr (WRITE_T || MODE == F8LIN_DELAYED) __syncthreads();
+
+  if constexpr (MODE == F8LIN_DELAYED) {
+    if (t == 0) {
+      uint32_t m = red[0];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+      atomicMax(reinterpret_cast<uint32_t *>(amax_acc), m << 16);
+    }
+  }
+
+  if constexpr (WRITE_T) {
+    const int k = t & 7;   // 16-row group of the tile
+    const int g = t >> 3;  // 4-column group of the tile
+    const int64_t qrow = col0 + 4 * g;  // first of the four qt rows
+    const int64_t qcol = row0 + 16 * k;
+    uint32_t d[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d[i] = tile[lds_word(16 * k + i, g)];
+    u32x4 out[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t e0, e1, e2, e3;
+      transpose4x4(d[4 * m], d[4 * m + 1], d[4 * m + 2], d[4 * m + 3], e0, e1, e2, e3);
+      out[0][m] = e0;
+      out[1][m] = e1;
+      out[2][m] = e2;
+      out[3][m] = e3;
+    }
+    if (qrow < cols && qcol < rows) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4 *>(qt + (qrow + b) * rows + qcol) = out[b];
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void cast_f32_kernel(const float *__restrict__ v, int64_t n,
+                                                            uint8_t *__restrict__ q) {
+  constexpr float fm = fmt_max<FMT>();
+  const int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 f = *reinterpret_cast<const float4 *>(v + i);
+    *reinterpret_cast<uint32_t *>(q + i) =
+        cvt4<FMT>(saturate(f.x, fm), saturate(f.y, fm), saturate(f.z, fm), saturate(f.w, fm));
+  } else {
+    for (int64_t j = i; j < n; ++j) q[j] = (uint8_t)(cvt4<FMT>(saturate(v[j], fm), 0.f, 0.f, 0.f) & 0xFFu);
+  }
+}
+
+template <int FMT, int MODE>
+void launch_ct(unsigned grid, int tiles_x, const uint16_t *x, int64_t rows, int64_t cols, const f8lin_state &st,
+               uint8_t *q, uint8_t *qt, hipStream_t stream) {
+  if (qt)
+    cast_transpose_kernel<FMT, MODE, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, st.amax, st.history,
+                                                                           st.amax, st.scale, q, qt, tiles_x);
+  else
+    cast_transpose_kernel<FMT, MODE, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, st.amax, st.history,
+                                                                            st.amax, st.scale, q, qt, tiles_x);
+}
+
+}  // namespace
+
+hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
+                                 const f8lin_state &st, uint8_t *q, uint8_t *qt, hipStream_t stream) {
+  // At least one workgroup even for an empty tensor: it still publishes the scale.
+  // (The C-ABI layer bounds rows * cols, so the tile count fits a 1-D grid.)
+  const int64_t gx = cols > 0 ? (cols + kTile - 1) / kTile : 1;
+  const int64_t gy = rows > 0 ? (rows + kTile - 1) / kTile : 1;
+  const unsigned grid = (unsigned)(gx * gy);
+  const int tx = (int)gx;
+  if (fmt == F8LIN_E4M3) {
+    if (mode == F8LIN_DYNAMIC) launch_ct<0, F8LIN_DYNAMIC>(grid, tx, x, rows, cols, st, q, qt, stream);
+    else launch_ct<0, F8LIN_DELAYED>(grid, tx, x, rows, cols, st, q, qt, stream);
+  } else {
+    if (mode == F8LIN_DYNAMIC) launch_ct<1, F8LIN_DYNAMIC>(grid, tx, x, rows, cols, st, q, qt, stream);
+    else launch_ct<1, F8LIN_DELAYED>(grid, tx, x, rows, cols, st, q, qt, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 4 * kThreads - 1) / (4 * kThreads);
+  if (fmt == F8LIN_E4M3)
+    cast_f32_kernel<0><<<(unsigned)blocks, kThreads, 0, stream>>>(v, n, q);
+  else
+    cast_f32_kernel<1><<<(unsigned)blocks, kThreads, 0, stream>>>(v, n, q);
+  return hipGetLastError();
+}
+
+}  // namespace f8lin

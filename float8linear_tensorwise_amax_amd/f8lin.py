@@ -1,0 +1,242 @@
+"""Thin Python binding of libf8lin.so (include/f8lin.h), same names as the C ABI.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory (tensors) and streams; this module
+checks dtypes / devices / contiguity, passes raw pointers and the current HIP
+stream, and raises F8linError on a non-zero status.  Importing it fails
+loudly if the library is not built -- there is no fallback.
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libf8lin.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "from the repository root")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+E4M3 = 0
+E5M2 = 1
+AMAX_ATOMIC = 0
+AMAX_TWOPASS = 1
+DYNAMIC = 0
+DELAYED = 1
+HISTORY_LEN = 16
+
+_FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+_ALGO = {"atomic": AMAX_ATOMIC, "twopass": AMAX_TWOPASS, AMAX_ATOMIC: AMAX_ATOMIC, AMAX_TWOPASS: AMAX_TWOPASS}
+_MODE = {"dynamic": DYNAMIC, "delayed": DELAYED, DYNAMIC: DYNAMIC, DELAYED: DELAYED}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+class State(ctypes.Structure):
+    _fields_ = [("amax", _vp), ("scale", _vp), ("history", _vp), ("hist_meta", _vp)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("x", _vp), ("w", _vp), ("y", _vp),
+                ("x8", _vp), ("x8t", _vp), ("w8", _vp), ("w8t", _vp), ("sx", State), ("sw", State),
+                ("mode_x", _int), ("mode_w", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("dy", _vp), ("x8t", _vp), ("w8t", _vp),
+                ("dx", _vp), ("dw", _vp), ("dy8", _vp), ("dy8t", _vp), ("sx", State), ("sw", State),
+                ("sdy", State), ("mode_dy", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
+
+
+_lib.f8lin_workspace_bytes.argtypes = []
+_lib.f8lin_workspace_bytes.restype = ctypes.c_size_t
+_lib.f8lin_status_str.argtypes = [_int]
+_lib.f8lin_status_str.restype = ctypes.c_char_p
+_lib.f8lin_amax.argtypes = [_vp, _i64, _int, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.f8lin_cast_transpose.argtypes = [_vp, _i64, _i64, _int, _int, ctypes.POINTER(State), _vp, _vp, _vp]
+_lib.f8lin_cast_f32.argtypes = [_vp, _i64, _int, _vp, _vp]
+_lib.f8lin_gemm.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+_lib.f8lin_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+_lib.f8lin_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+_lib.f8lin_delayed_update.argtypes = [ctypes.POINTER(State), _int, _vp]
+for _name in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_cast_f32", "f8lin_gemm", "f8lin_forward",
+              "f8lin_backward", "f8lin_delayed_update"):
+    getattr(_lib, _name).restype = _int
+
+
+class F8linError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(_lib.f8lin_status_str(status).decode())
+
+
+def _check(status: int):
+    if status != 0:
+        raise F8linError(status)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("f8lin: tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("f8lin: tensors must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"f8lin: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def workspace_bytes() -> int:
+    return int(_lib.f8lin_workspace_bytes())
+
+
+def status_str(status: int) -> str:
+    return _lib.f8lin_status_str(status).decode()
+
+
+def new_workspace(device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (uint8) of workspace_bytes()."""
+    return torch.zeros(workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+class ScalingState:
+    """Device-resident scaling state of one tensor role (f8lin_state):
+    amax [1] f32, scale [2] f32 = {scale, 1/scale}, history [16] f32,
+    hist_meta [2] i32 = {count, pos}; all zero-initialised."""
+
+    def __init__(self, device="cuda"):
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self.scale = torch.zeros(2, dtype=torch.float32, device=device)
+        self.history = torch.zeros(HISTORY_LEN, dtype=torch.float32, device=device)
+        self.hist_meta = torch.zeros(2, dtype=torch.int32, device=device)
+
+    def c_struct(self) -> State:
+        return State(self.amax.data_ptr(), self.scale.data_ptr(), self.history.data_ptr(), self.hist_meta.data_ptr())
+
+    @property
+    def inv_scale(self) -> torch.Tensor:
+        return self.scale[1:2]
+
+    def state_dict(self):
+        """Host copies of the state (for checkpointing)."""
+        return {k: getattr(self, k).detach().cpu().clone() for k in ("amax", "scale", "history", "hist_meta")}
+
+    def load_state_dict(self, sd):
+        for k in ("amax", "scale", "history", "hist_meta"):
+            getattr(self, k).copy_(sd[k])
+
+
+# ----------------------------------------------------------------- entry points
+
+def amax(x: torch.Tensor, out: torch.Tensor, ws: torch.Tensor, algo="atomic", stream=None):
+    _check(_lib.f8lin_amax(_ptr(x, torch.bfloat16), x.numel(), _ALGO[algo], _ptr(out, torch.float32),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def cast_transpose(x: torch.Tensor, fmt, mode, state: ScalingState, q: torch.Tensor,
+                   qt: Optional[torch.Tensor] = None, stream=None):
+    if x.dim() != 2:
+        raise ValueError("cast_transpose takes a 2-D tensor")
+    st = state.c_struct()
+    _check(_lib.f8lin_cast_transpose(_ptr(x, torch.bfloat16), x.shape[0], x.shape[1], _FMT[fmt], _MODE[mode],
+                                     ctypes.byref(st), _ptr(q, torch.uint8), _ptr(qt, torch.uint8),
+                                     _stream(stream)))
+
+
+def cast_f32(v: torch.Tensor, fmt, q: torch.Tensor, stream=None):
+    _check(_lib.f8lin_cast_f32(_ptr(v, torch.float32), v.numel(), _FMT[fmt], _ptr(q, torch.uint8),
+                               _stream(stream)))
+
+
+def gemm(a: torch.Tensor, fmt_a, b: torch.Tensor, fmt_b, inv_a: torch.Tensor, inv_b: torch.Tensor,
+         c: torch.Tensor, stream=None):
+    """c (M, N) bf16 = a (M, K) . b (N, K)^T * inv_a[0] * inv_b[0]."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(c.shape) != (M, N):
+        raise ValueError("gemm: shape mismatch")
+    _check(_lib.f8lin_gemm(_ptr(a, torch.uint8), _FMT[fmt_a], _ptr(b, torch.uint8), _FMT[fmt_b], M, N, K,
+                           _ptr(inv_a, torch.float32), _ptr(inv_b, torch.float32), _ptr(c, torch.bfloat16),
+                           _stream(stream)))
+
+
+def forward(x, w, y, x8, x8t, w8, w8t, sx: ScalingState, sw: ScalingState, ws, mode_x="dynamic",
+            mode_w="dynamic", algo="atomic", stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    a = FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
+                _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
+                sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
+                ws.numel() * ws.element_size())
+    if w.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("forward: shape mismatch")
+    _check(_lib.f8lin_forward(ctypes.byref(a), _stream(stream)))
+
+
+def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState, sdy: ScalingState, ws,
+             mode_dy="dynamic", algo="atomic", stream=None):
+    M, N = dy.shape
+    K = x8t.shape[0]
+    if tuple(dx.shape) != (M, K) or tuple(dw.shape) != (N, K) or tuple(w8t.shape) != (K, N):
+        raise ValueError("backward: shape mismatch")
+    a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr(x8t, torch.uint8), _ptr(w8t, torch.uint8),
+                _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr(dy8t, torch.uint8),
+                sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], _ptr(ws),
+                ws.numel() * ws.element_size())
+    _check(_lib.f8lin_backward(ctypes.byref(a), _stream(stream)))
+
+
+def delayed_update(states: Sequence[ScalingState], stream=None):
+    arr = (State * max(1, len(states)))(*[s.c_struct() for s in states])
+    _check(_lib.f8lin_delayed_update(arr, len(states), _stream(stream)))
+
+
+# ------------------------------------------------------------ layer buffers
+
+class LinearBuffers:
+    """Every device buffer one Float8Linear forward + backward needs, for
+    X (M, K), W (N, K), dY (M, N); allocated once with torch (plumbing)."""
+
+    def __init__(self, M: int, N: int, K: int, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.M, self.N, self.K = M, N, K
+        self.y = torch.empty((M, N), **bf)
+        self.dx = torch.empty((M, K), **bf)
+        self.dw = torch.empty((N, K), **bf)
+        self.x8 = torch.empty((M, K), **u8)
+        self.x8t = torch.empty((K, M), **u8)
+        self.w8 = torch.empty((N, K), **u8)
+        self.w8t = torch.empty((K, N), **u8)
+        self.dy8 = torch.empty((M, N), **u8)
+        self.dy8t = torch.empty((N, M), **u8)
+        self.sx = ScalingState(device)
+        self.sw = ScalingState(device)
+        self.sdy = ScalingState(device)
+        self.ws = new_workspace(device)
+
+    def forward(self, x, w, mode="dynamic", algo="atomic", stream=None):
+        forward(x, w, self.y, self.x8, self.x8t, self.w8, self.w8t, self.sx, self.sw, self.ws, mode, mode, algo,
+                stream)
+        return self.y
+
+    def backward(self, dy, mode="dynamic", algo="atomic", stream=None):
+        backward(dy, self.x8t, self.w8t, self.dx, self.dw, self.dy8, self.dy8t, self.sx, self.sw, self.sdy,
+                 self.ws, mode, algo, stream)
+        return self.dx, self.dw
+
+    def states(self):
+        return [self.sx, self.sw, self.sdy]

@@ -1,0 +1,184 @@
+/*
+ * f8lin.h -- C ABI of libf8lin.so, the MI355X (gfx950) Float8Linear library:
+ * forward and backward of a linear layer Y = X W^T whose three GEMMs run in
+ * fp8 with tensorwise scaling.
+ *
+ * What the library computes, with where it comes from:
+ *  - Tensorwise dynamic scaling: one scale per tensor, from that tensor's
+ *    current absolute maximum (amax), computed on the fly (pytorch/torchtitan
+ *    PR #778 "Integrate float8nocompile", Summary).  The amax is computed by
+ *    one of two algorithms that the PR's single-linear-layer benchmark table
+ *    compares as kernel_algo ATOMIC_MAX and REDUCTION.
+ *  - Delayed scaling of input, weight and grad_output: the scale comes from
+ *    an amax history of past steps, updated after backward
+ *    (pytorch/ao issue #1297, repro script: Float8LinearConfig with
+ *    ScalingType.DELAYED, and sync_float8_amax_and_scale_history after
+ *    loss.backward()).
+ *  - The measured unit is the forward + backward of one linear layer
+ *    (PR #778, "Benchmarking single linear layer forward+backward").
+ * The arithmetic itself is not written on those pages; this library fixes
+ * it as follows (the same definitions the tests check bit for bit):
+ *    amax  = max_i |x_i|                   (exact; 0 for an empty tensor)
+ *    scale = fmax / max(amax, 1e-12)       (IEEE binary32, correctly rounded)
+ *    q     = RNE_sat(fl32(x * scale))      (binary32 multiply, then clamp to
+ *                                           +-fmax, then round to nearest even
+ *                                           onto the OCP fp8 grid; -0 stays -0;
+ *                                           subnormals kept; NaN -> a NaN code)
+ *    fmax  = 448 for OCP E4M3 (X, W), 57344 for OCP E5M2 (dY)
+ *    Y  = (X8 W8^T)  / (s_x  s_w)   bf16, fp32 accumulation
+ *    dX = (dY8 W8)   / (s_dy s_w)   bf16
+ *    dW = (dY8^T X8) / (s_dy s_x)   bf16
+ *
+ * Conventions for every entry point:
+ *  - Every data pointer is a DEVICE pointer owned by the caller, 16-byte
+ *    aligned, to a row-major contiguous tensor.  bf16 tensors are passed as
+ *    their uint16_t bit patterns; fp8 tensors as uint8_t codes.  A data
+ *    pointer may be NULL only if its tensor has no elements.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it: nothing synchronises, nothing is read back to the
+ *    host, nothing is allocated, and no pointer is kept after the call.
+ *  - Matrix dimensions (rows, cols, M, N, K) must be >= 0 and multiples of
+ *    16 (every row is then a whole number of 16-byte vectors in both the
+ *    row-major and the transposed layout).  A zero dimension is allowed and
+ *    computes the degenerate result (e.g. dW = 0 when M = 0).
+ *  - Arguments are checked before anything is launched; on error nothing is
+ *    enqueued and a non-zero f8lin_status is returned.  F8LIN_EHIP reports a
+ *    failed launch (hipGetLastError); faults during execution surface at the
+ *    caller's next synchronisation.  Data-dependent conditions (NaN, Inf)
+ *    are not errors.
+ *  - Calls that share a workspace or a scaling state must be ordered (same
+ *    stream, or synchronised); the library keeps no global mutable state.
+ */
+#ifndef F8LIN_H_
+#define F8LIN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  F8LIN_OK = 0,
+  F8LIN_EINVAL = 1,     /* null pointer, bad enum, overlapping buffers, bad count */
+  F8LIN_ESHAPE = 2,     /* negative dimension, or not a multiple of 16 */
+  F8LIN_EALIGN = 3,     /* a pointer not 16-byte aligned */
+  F8LIN_EWORKSPACE = 4, /* workspace missing or smaller than f8lin_workspace_bytes() */
+  F8LIN_EHIP = 5        /* a HIP launch failed */
+} f8lin_status;
+
+typedef enum { F8LIN_E4M3 = 0, F8LIN_E5M2 = 1 } f8lin_fmt;
+
+/* The two amax algorithms of the single-linear benchmark (PR #778 table):
+ * ATOMIC: every workgroup reduces its share and folds it into one global
+ *         slot with an atomic max (one launch).
+ * TWOPASS: every workgroup writes its partial max; a second one-workgroup
+ *          launch reduces the partials. */
+typedef enum { F8LIN_AMAX_ATOMIC = 0, F8LIN_AMAX_TWOPASS = 1 } f8lin_amax_algo;
+
+/* DYNAMIC: the scale comes from state->amax, written beforehand by
+ *          f8lin_amax for the same tensor.
+ * DELAYED: the scale comes from max(state->history[0..15]) (past steps only),
+ *          and the cast also folds this tensor's amax into state->amax
+ *          (which must hold 0 or a smaller value: f8lin_delayed_update resets
+ *          it).  A role's first step has no history; callers run it in
+ *          DYNAMIC mode (amax initialisation) and then call
+ *          f8lin_delayed_update, which records it. */
+typedef enum { F8LIN_DYNAMIC = 0, F8LIN_DELAYED = 1 } f8lin_scaling;
+
+#define F8LIN_HISTORY_LEN 16
+
+/* Scaling state of one tensor role (input, weight or grad_output); all
+ * device pointers, caller-owned, zero-initialised before first use. */
+typedef struct {
+  float *amax;        /* [1] amax of the tensor (dynamic: written by f8lin_amax;
+                         delayed: this step's amax, accumulated by the cast) */
+  float *scale;       /* [2] written by the cast: {scale, 1/scale} */
+  float *history;     /* [16] delayed only (may be NULL in dynamic mode) */
+  int32_t *hist_meta; /* [2] delayed only: {count (0..16), pos (0..15)} */
+} f8lin_state;
+
+/* Bytes of device workspace that f8lin_amax / f8lin_forward /
+ * f8lin_backward need (a constant).  The caller zero-fills it once before
+ * first use; every call leaves it zero-filled again. */
+size_t f8lin_workspace_bytes(void);
+
+/* Human-readable name of a status code (static string). */
+const char *f8lin_status_str(int status);
+
+/* amax of a bf16 tensor of n elements -> amax_out[0] (fp32).  The result is
+ * exact (it is one of the inputs' magnitudes), the same for both algorithms
+ * and for every launch order; NaN inputs make it NaN; n = 0 gives 0.
+ * algo: f8lin_amax_algo.  ws: workspace of >= f8lin_workspace_bytes(). */
+int f8lin_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* Scale and cast of a bf16 (rows, cols) tensor to fp8 codes q (rows, cols),
+ * and, if qt != NULL, the transposed copy qt (cols, rows), in one pass.
+ * fmt: f8lin_fmt.  mode: f8lin_scaling (see above).  The scale and inverse
+ * scale the cast used are stored to st->scale[0..1]. */
+int f8lin_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
+                         const f8lin_state *st, uint8_t *q, uint8_t *qt, void *stream);
+
+/* The conversion alone, on fp32 values (scale 1): q[i] = RNE_sat(v[i]). */
+int f8lin_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, void *stream);
+
+/* fp8 GEMM with a per-tensor dequantisation epilogue:
+ *   C (M, N) bf16 = (A (M, K) . B (N, K)^T) * inv_scale_a[0] * inv_scale_b[0]
+ * A and B are fp8 codes in formats fmt_a / fmt_b, both contiguous along K;
+ * products are exact and accumulate in fp32; the result is rounded once to
+ * bf16 (nearest even) after the scaling.  K = 0 gives C = 0. */
+int f8lin_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t M, int64_t N, int64_t K,
+               const float *inv_scale_a, const float *inv_scale_b, uint16_t *c, void *stream);
+
+/* Forward of the layer: X (M, K) bf16, W (N, K) bf16 -> Y (M, N) bf16.
+ * Per tensor: amax (dynamic mode only), then one cast writing both layouts;
+ * then Y = X8 . W8^T with the dequantisation epilogue.  x8t and w8t (and the
+ * scales in sx, sw) are what backward needs; x8 and w8 can be reused or
+ * freed after the call. */
+typedef struct {
+  int64_t M, N, K;
+  const uint16_t *x, *w; /* inputs */
+  uint16_t *y;           /* output (M, N) */
+  uint8_t *x8, *x8t;     /* (M, K) e4m3 and its transpose (K, M) */
+  uint8_t *w8, *w8t;     /* (N, K) e4m3 and its transpose (K, N) */
+  f8lin_state sx, sw;
+  int mode_x, mode_w; /* f8lin_scaling */
+  int algo;           /* f8lin_amax_algo, for the dynamic-mode amax passes */
+  void *ws;
+  size_t ws_bytes;
+} f8lin_fwd_args;
+
+/* Backward of the layer, given dY (M, N) bf16 and the forward's saved x8t,
+ * w8t and scaling states: dY is cast once to e5m2 (both layouts), then
+ * dX (M, K) = dY8 . W8 (contraction over N, B operand w8t) and
+ * dW (N, K) = dY8^T . X8 (contraction over M, A operand dy8t, B operand x8t),
+ * each with its dequantisation epilogue. */
+typedef struct {
+  int64_t M, N, K;
+  const uint16_t *dy;           /* input (M, N) */
+  const uint8_t *x8t, *w8t;     /* saved by forward: (K, M), (K, N) */
+  uint16_t *dx, *dw;            /* outputs (M, K), (N, K) */
+  uint8_t *dy8, *dy8t;          /* (M, N) e5m2 and its transpose (N, M) */
+  f8lin_state sx, sw, sdy;      /* sx, sw: the forward's states (scales read) */
+  int mode_dy;                  /* f8lin_scaling */
+  int algo;                     /* f8lin_amax_algo */
+  void *ws;
+  size_t ws_bytes;
+} f8lin_bwd_args;
+
+int f8lin_forward(const f8lin_fwd_args *args, void *stream);
+int f8lin_backward(const f8lin_bwd_args *args, void *stream);
+
+/* After backward (the sync step of delayed scaling), for each of the
+ * n_states states: history[pos] = amax; pos = (pos + 1) % 16;
+ * count = min(count + 1, 16); amax = 0.  Every state needs history and
+ * hist_meta. */
+int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* F8LIN_H_ */

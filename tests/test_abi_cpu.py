@@ -1,0 +1,164 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every function
+include/f8lin.h declares, and rejects bad arguments before launching anything
+(these calls return from host-side validation and touch no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "libf8lin.so")
+HEADER_DIR = os.path.join(ROOT, "include")
+
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE = 0, 1, 2, 3, 4
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(HEADER_DIR):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(f8lin_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libf8lin.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_forward", "f8lin_backward",
+                     "f8lin_delayed_update", "f8lin_gemm", "f8lin_cast_f32", "f8lin_workspace_bytes",
+                     "f8lin_status_str"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_and_status_strings(lib):
+    lib.f8lin_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.f8lin_workspace_bytes() >= 4096
+    lib.f8lin_status_str.restype = ctypes.c_char_p
+    lib.f8lin_status_str.argtypes = [ctypes.c_int]
+    for code in range(6):
+        assert lib.f8lin_status_str(code).startswith(b"F8LIN_")
+    assert b"unknown" in lib.f8lin_status_str(99)
+
+
+class State(ctypes.Structure):
+    _fields_ = [("amax", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("history", ctypes.c_void_p),
+                ("hist_meta", ctypes.c_void_p)]
+
+
+# Fake, never-dereferenced addresses: validation rejects before any launch.
+A = 0x10000000
+B = 0x20000000
+C = 0x30000000
+WS = 0x40000000
+AMAX = 0x50000000
+SCALE = 0x50000100
+HIST = 0x50000200
+META = 0x50000300
+
+
+def test_amax_rejections(lib):
+    f = lib.f8lin_amax
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(A, 64, 0, None, WS, 8192, None) == EINVAL          # no output
+    assert f(None, 64, 0, AMAX, WS, 8192, None) == EINVAL       # no input with elements
+    assert f(A, 64, 2, AMAX, WS, 8192, None) == EINVAL          # bad algorithm
+    assert f(A, -1, 0, AMAX, WS, 8192, None) == ESHAPE
+    assert f(A + 2, 64, 0, AMAX, WS, 8192, None) == EALIGN
+    assert f(A, 64, 0, AMAX, None, 8192, None) == EWORKSPACE
+    assert f(A, 64, 0, AMAX, WS, 16, None) == EWORKSPACE
+    assert f(A, 64, 1, AMAX, WS + 8, 8192, None) == EWORKSPACE   # misaligned workspace
+    assert f(A, 64, 0, A + 16, WS, 8192, None) == EINVAL       # output inside the input
+
+
+def test_cast_rejections(lib):
+    f = lib.f8lin_cast_transpose
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(State), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    st = State(AMAX, SCALE, None, None)
+    dst = State(AMAX, SCALE, HIST, META)
+    assert f(A, 32, 48, 0, 0, None, B, C, None) == EINVAL        # no state
+    assert f(A, 32, 48, 2, 0, ctypes.byref(st), B, C, None) == EINVAL
+    assert f(A, 32, 48, 0, 5, ctypes.byref(st), B, C, None) == EINVAL
+    assert f(A, 32, 48, 0, 1, ctypes.byref(st), B, C, None) == EINVAL  # delayed without history
+    assert f(A, 33, 48, 0, 0, ctypes.byref(st), B, C, None) == ESHAPE
+    assert f(A, 32, 40, 0, 0, ctypes.byref(st), B, C, None) == ESHAPE
+    assert f(A, -16, 48, 0, 0, ctypes.byref(st), B, C, None) == ESHAPE
+    assert f(A, 32, 48, 0, 0, ctypes.byref(st), B + 1, C, None) == EALIGN
+    assert f(A, 32, 48, 0, 0, ctypes.byref(st), B, C + 8, None) == EALIGN
+    assert f(A, 32, 48, 0, 0, ctypes.byref(st), B, B + 512, None) == EINVAL  # q and qt overlap
+    assert f(A, 32, 48, 0, 0, ctypes.byref(st), A + 1024, C, None) == EINVAL  # q inside x
+    bad = State(AMAX, AMAX, None, None)  # scale overlaps amax
+    assert f(A, 32, 48, 0, 0, ctypes.byref(bad), B, C, None) == EINVAL
+    assert f(None, 32, 48, 0, 1, ctypes.byref(dst), B, C, None) == EINVAL
+
+
+def test_gemm_rejections(lib):
+    f = lib.f8lin_gemm
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(A, 0, B, 0, 32, 48, 64, None, SCALE, C, None) == EINVAL
+    assert f(A, 0, B, 3, 32, 48, 64, AMAX, SCALE, C, None) == EINVAL
+    assert f(A, 0, B, 0, 32, 48, 65, AMAX, SCALE, C, None) == ESHAPE
+    assert f(A, 0, B, 0, 1 << 31, 48, 64, AMAX, SCALE, C, None) == ESHAPE
+    assert f(A, 0, B + 4, 0, 32, 48, 64, AMAX, SCALE, C, None) == EALIGN
+    assert f(A, 0, B, 0, 32, 48, 64, AMAX, SCALE, A, None) == EINVAL   # C aliases A
+    assert f(None, 0, B, 0, 32, 48, 64, AMAX, SCALE, C, None) == EINVAL
+
+
+class Fwd(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)] + \
+               [(n, ctypes.c_void_p) for n in ("x", "w", "y", "x8", "x8t", "w8", "w8t")] + \
+               [("sx", State), ("sw", State), ("mode_x", ctypes.c_int), ("mode_w", ctypes.c_int),
+                ("algo", ctypes.c_int), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def test_forward_rejections(lib):
+    f = lib.f8lin_forward
+    f.argtypes = [ctypes.POINTER(Fwd), ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    MB = 1 << 20
+
+    def args(**kw):
+        a = Fwd(32, 48, 64, A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB,
+                State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None), 0, 0, 0, WS, 8192)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    assert f(None, None) == EINVAL
+    assert f(ctypes.byref(args(K=63)), None) == ESHAPE
+    assert f(ctypes.byref(args(mode_w=7)), None) == EINVAL
+    assert f(ctypes.byref(args(y=A + 2 * MB + 2)), None) == EALIGN
+    assert f(ctypes.byref(args(ws_bytes=100)), None) == EWORKSPACE
+    assert f(ctypes.byref(args(w8=A + 3 * MB)), None) == EINVAL  # w8 aliases x8
+    assert f(ctypes.byref(args(sw=State(AMAX, SCALE + 64, None, None))), None) == EINVAL  # shared amax slot
+    assert f(ctypes.byref(args(mode_x=1)), None) == EINVAL  # delayed without history
+
+
+def test_delayed_update_rejections(lib):
+    f = lib.f8lin_delayed_update
+    f.argtypes = [ctypes.POINTER(State), ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    arr = (State * 2)(State(AMAX, SCALE, HIST, META), State(AMAX, SCALE, None, META))
+    assert f(arr, 2, None) == EINVAL
+    assert f(arr, -1, None) == EINVAL
+    arr2 = (State * 1)(State(AMAX, SCALE, HIST + 4, META))
+    assert f(arr2, 1, None) == EALIGN

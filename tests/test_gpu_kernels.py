@@ -1,0 +1,255 @@
+"""Kernel-level parity of the HIP path against the CPU oracle, through the C ABI.
+
+amax (both algorithms), scale, the fp8 conversion and the fused cast +
+transpose must match the oracle bit for bit; the GEMM must meet the
+tolerance (and be bit-exact where the arithmetic is exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from float8linear_tensorwise_amax_amd import inputs
+from helpers import bits, bf16_to_f64, f32_bits, gemm_check, np_f32_bits, u8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+FMTS = [oracle.E4M3, oracle.E5M2]
+
+
+@pytest.fixture(scope="module")
+def f8():
+    from float8linear_tensorwise_amax_amd import f8lin
+    return f8lin
+
+
+def _amax_gpu(f8, x_dev, algo):
+    out = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    ws = f8.new_workspace(DEV)
+    f8.amax(x_dev.reshape(-1), out, ws, algo)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws).item() == 0  # the workspace is left zero-filled
+    return out
+
+
+# ------------------------------------------------------------------ amax
+
+@pytest.mark.parametrize("algo", ["atomic", "twopass"])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4095, 65536, 1_000_003, 16 * 4096 * 4 + 5, 64 * 1024 * 1024 + 24])
+def test_amax_matches_oracle(f8, algo, n):
+    print(f"amax algo={algo} n={n}", flush=True)
+    x = inputs.random_bf16((n,), seed=n, std=3.0)
+    # plant the maximum at the very end and a large negative near the start
+    if n >= 2:
+        x[-1] = 1000.0
+        x[1] = -999.0
+    got = _amax_gpu(f8, x.to(DEV), algo)
+    want = oracle.amax(bits(x))
+    assert f32_bits(got)[0] == np_f32_bits(want)
+
+
+@pytest.mark.parametrize("algo", ["atomic", "twopass"])
+def test_amax_special_values(f8, algo):
+    cases = {
+        "neg_zero": torch.tensor([-0.0] * 16, dtype=torch.bfloat16),
+        "subnormal": torch.from_numpy(np.array([0, 0x0003, 0x8005, 0x0001] * 4, dtype=np.uint16).view(np.int16))
+        .view(torch.bfloat16),
+        "neg_only": torch.tensor([-1.0, -3.0, -2.0] * 8, dtype=torch.bfloat16),
+        "inf": torch.tensor([1.0, float("-inf"), 2.0] * 8, dtype=torch.bfloat16),
+    }
+    for name, x in cases.items():
+        got = _amax_gpu(f8, x.to(DEV), algo)
+        assert f32_bits(got)[0] == np_f32_bits(oracle.amax(bits(x))), name
+    x = torch.tensor([1.0, float("nan"), 2.0] * 8, dtype=torch.bfloat16)
+    assert torch.isnan(_amax_gpu(f8, x.to(DEV), algo)).item()
+
+
+def test_amax_algorithms_agree_and_repeat(f8):
+    x = inputs.random_bf16((4096, 4096), seed=11).to(DEV)
+    a = [f32_bits(_amax_gpu(f8, x, algo))[0] for algo in ("atomic", "twopass", "atomic", "twopass")]
+    assert len(set(a)) == 1
+
+
+# --------------------------------------------------------- fp8 conversion
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_conversion_exhaustive_nonnegative(f8, fmt):
+    """Every non-negative binary32 pattern up to 2 * fmax (larger values only
+    saturate), through the device conversion, against the oracle."""
+    hi = int(np.float32(2 * oracle.FMAX[fmt]).view(np.uint32))
+    chunk = 1 << 26
+    q = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    for lo in range(0, hi, chunk):
+        n = min(chunk, hi - lo)
+        v = torch.arange(lo, lo + n, dtype=torch.int64, device=DEV).to(torch.int32).view(torch.float32)
+        f8.cast_f32(v, fmt, q[:n])
+        want = oracle.encode_bits_range(lo, n, fmt)
+        got = u8(q[:n])
+        if not np.array_equal(got, want):
+            bad = np.nonzero(got != want)[0][:5]
+            raise AssertionError(f"fmt {fmt}: mismatch at {[hex(lo + int(b)) for b in bad]}: "
+                                 f"got {[hex(got[b]) for b in bad]} want {[hex(want[b]) for b in bad]}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_conversion_random_patterns_and_sign(f8, fmt):
+    rng = np.random.default_rng(100 + fmt)
+    b = rng.integers(0, 2 ** 32, size=1 << 24, dtype=np.uint64).astype(np.uint32)
+    v = b.view(np.float32)
+    v = np.ascontiguousarray(v[~np.isnan(v)])
+    q = torch.empty(v.size, dtype=torch.uint8, device=DEV)
+    f8.cast_f32(torch.from_numpy(v).to(DEV), fmt, q)
+    assert np.array_equal(u8(q), oracle.encode_f32(v, fmt))
+    # NaN inputs give some NaN code
+    nan = torch.full((16,), float("nan"), device=DEV)
+    qn = torch.empty(16, dtype=torch.uint8, device=DEV)
+    f8.cast_f32(nan, fmt, qn)
+    assert np.all(np.isnan(oracle.decode(u8(qn), fmt)))
+
+
+# --------------------------------------------------------- cast + transpose
+
+def _cast_gpu(f8, x_dev, fmt, mode="dynamic", state=None, amax_value=None, transpose=True):
+    rows, cols = x_dev.shape
+    st = state or f8.ScalingState(DEV)
+    if amax_value is not None:
+        st.amax.fill_(float(amax_value))
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=DEV) if transpose else None
+    f8.cast_transpose(x_dev, fmt, mode, st, q, qt)
+    torch.cuda.synchronize()
+    return st, q, qt
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(16, 16), (16, 4096), (48, 160), (128, 128), (144, 272), (400, 1600),
+                                   (1024, 4800), (4096, 4096)])
+def test_cast_transpose_dynamic_matches_oracle(f8, fmt, shape):
+    print(f"cast fmt={fmt} shape={shape}", flush=True)
+    x = inputs.random_bf16(shape, seed=shape[0] * 7 + shape[1], std=2.0)
+    xd = x.to(DEV)
+    st = f8.ScalingState(DEV)
+    ws = f8.new_workspace(DEV)
+    f8.amax(xd.reshape(-1), st.amax, ws)
+    st, q, qt = _cast_gpu(f8, xd, fmt, state=st)
+    a = oracle.amax(bits(x))
+    s, inv = oracle.scale(a, fmt)
+    rq, rqt, _ = oracle.cast(bits(x), fmt, s)
+    assert f32_bits(st.amax)[0] == np_f32_bits(a)
+    assert f32_bits(st.scale)[0] == np_f32_bits(s) and f32_bits(st.scale)[1] == np_f32_bits(inv)
+    assert np.array_equal(u8(q), rq)
+    assert np.array_equal(u8(qt), rqt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cast_without_transpose(f8, fmt):
+    x = inputs.random_bf16((272, 144), seed=5)
+    _, q, _ = _cast_gpu(f8, x.to(DEV), fmt, amax_value=1.5, transpose=False)
+    s, _ = oracle.scale(np.float32(1.5), fmt)  # a stale amax: saturation exercised
+    rq, _, nsat = oracle.cast(bits(x), fmt, s)
+    assert nsat > 0 and np.array_equal(u8(q), rq)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cast_every_bf16_value_under_many_scales(f8, fmt):
+    """All 65536 bf16 patterns (NaN ones give some NaN code) cast under scales
+    from a spread of amax values, including tiny, huge, eps-clamped and
+    power-of-two ones: bytes and scales must equal the oracle's."""
+    allb = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).reshape(256, 256)
+    xd = allb.to(DEV)
+    xb = bits(allb)
+    nan_mask = np.isnan((xb.astype(np.uint32) << 16).view(np.float32))
+    mags = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    amaxes = list(mags[::61]) + [0.0, 1e-30, 3.5, 448.0, 57344.0, 0.1259765625, float(mags[-1])]
+    for a in amaxes:
+        st, q, qt = _cast_gpu(f8, xd, fmt, amax_value=a)
+        s, inv = oracle.scale(np.float32(a), fmt)
+        assert f32_bits(st.scale)[0] == np_f32_bits(s), a
+        assert f32_bits(st.scale)[1] == np_f32_bits(inv), a
+        rq, rqt, _ = oracle.cast(xb, fmt, s)
+        g = u8(q)
+        assert np.array_equal(g[~nan_mask], rq[~nan_mask]), a
+        assert np.all(np.isnan(oracle.decode(g[nan_mask], fmt)))
+        assert np.array_equal(u8(qt), g.T)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cast_delayed_mode_scale_and_fused_amax(f8, fmt):
+    x = inputs.random_bf16((400, 1600), seed=77, std=4.0)
+    xd = x.to(DEV)
+    st = f8.ScalingState(DEV)
+    hist = np.array([0.5, 3.0, 0.0, 7.25] + [0.0] * 12, dtype=np.float32)
+    st.history.copy_(torch.from_numpy(hist))
+    st.hist_meta.copy_(torch.tensor([4, 4], dtype=torch.int32))
+    st, q, qt = _cast_gpu(f8, xd, fmt, mode="delayed", state=st)
+    s, inv = oracle.scale(np.float32(7.25), fmt)
+    rq, rqt, _ = oracle.cast(bits(x), fmt, s)
+    assert f32_bits(st.scale)[0] == np_f32_bits(s)
+    assert np.array_equal(u8(q), rq) and np.array_equal(u8(qt), rqt)
+    assert f32_bits(st.amax)[0] == np_f32_bits(oracle.amax(bits(x)))  # fused amax of this step
+
+
+# ------------------------------------------------------------------- GEMM
+
+def _codes(rng, shape, fmt):
+    finite = [c for c in range(0x80) if np.isfinite(oracle.fp8_decode_scalar(c, fmt))]
+    c = rng.choice(finite, size=shape).astype(np.uint8)
+    return c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+
+def _gemm_gpu(f8, a, fa, b, fb, inv_a, inv_b):
+    M, N = a.shape[0], b.shape[0]
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ia = torch.tensor([inv_a], dtype=torch.float32, device=DEV)
+    ib = torch.tensor([inv_b], dtype=torch.float32, device=DEV)
+    f8.gemm(torch.from_numpy(a).to(DEV), fa, torch.from_numpy(b).to(DEV), fb, ia, ib, c)
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("mnk", [(16, 16, 16), (32, 48, 64), (128, 128, 128), (144, 272, 400), (16, 4096, 4096),
+                                 (256, 4800, 1600), (4096, 16, 16), (1024, 1024, 4096), (64, 80, 16)])
+def test_gemm_matches_oracle(f8, fa, fb, mnk):
+    M, N, K = mnk
+    print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + 3 * N + 7 * K + fa + 2 * fb)
+    a = _codes(rng, (M, K), fa)
+    b = _codes(rng, (N, K), fb)
+    # keep values moderate so fp32 accumulation is the only error source
+    a &= 0xF7 if fa == 0 else 0xF3
+    b &= 0xF7 if fb == 0 else 0xF3
+    sa, sb = np.float32(4.0), np.float32(0.125)
+    c = _gemm_gpu(f8, a, fa, b, fb, np.float32(1) / sa, np.float32(1) / sb)
+    A = oracle.decode(a, fa)
+    B = oracle.decode(b, fb)
+    ref = (A @ B.T) / np.float64(sa) / np.float64(sb)
+    gemm_check(bf16_to_f64(c), ref, what=f"gemm {mnk}")
+
+
+def test_gemm_integer_exact_is_bit_exact(f8):
+    """Small-integer operands at scale 1: every fp32 partial sum is exact, so
+    the bf16 result must be the exactly rounded integer product."""
+    rng = np.random.default_rng(3)
+    ints = {0: 0x00, 1: 0x38, -1: 0xB8, 2: 0x40, -2: 0xC0}
+    keys = np.array(list(ints))
+    for (M, N, K) in [(16, 48, 1600), (144, 4800, 16), (256, 256, 4096)]:
+        av = rng.choice(keys, (M, K))
+        bv = rng.choice(keys, (N, K))
+        a = np.vectorize(ints.get)(av).astype(np.uint8)
+        b = np.vectorize(ints.get)(bv).astype(np.uint8)
+        c = _gemm_gpu(f8, a, 0, b, 0, np.float32(1), np.float32(1))
+        exact = av.astype(np.int64) @ bv.T.astype(np.int64)
+        want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16)
+        assert torch.equal(c.cpu().view(torch.int16), want.view(torch.int16)), (M, N, K)
+
+
+def test_gemm_k_zero_gives_zeros(f8):
+    a = np.zeros((32, 0), dtype=np.uint8)
+    b = np.zeros((48, 0), dtype=np.uint8)
+    c = torch.full((32, 48), 7.0, dtype=torch.bfloat16, device=DEV)
+    ia = torch.ones(1, dtype=torch.float32, device=DEV)
+    f8.gemm(torch.from_numpy(a).to(DEV), 0, torch.from_numpy(b).to(DEV), 0, ia, ia, c)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(c).item() == 0
