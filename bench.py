@@ -108,28 +108,32 @@ def main():
     bufs = [f8lin.LinearBuffers(l.M, l.N, l.K, dev) for l in wl.linears]
     torch.cuda.synchronize()
 
-    def step(t):
+    def step(t, algo):
         mode = "delayed" if (delayed and t > 0) else "dynamic"
         for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
-            buf.forward(x, w, mode, args.algo)
-            buf.backward(dy, mode, args.algo)
+            buf.forward(x, w, mode, algo)
+            buf.backward(dy, mode, algo)
             if delayed:
                 f8lin.delayed_update(buf.states())
 
-    # ---- timed region
-    for t in range(args.warmup):
-        step(t)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t_host0 = time.perf_counter()
-    e0.record(stream)
-    for t in range(args.steps):
-        step(args.warmup + t)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    def timed_steps(algo):
+        for t in range(args.warmup):
+            step(t, algo)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t_host0 = time.perf_counter()
+        e0.record(stream)
+        for t in range(args.steps):
+            step(args.warmup + t, algo)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t_host0
+
+    # ---- timed region (the headline), then the same with the other amax algorithm
+    ms_per_step, t_host = timed_steps(args.algo)
+    other = "twopass" if args.algo == "atomic" else "atomic"
+    ms_other = None if (delayed or args.only_timed) else timed_steps(other)[0]
     flops = wl.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
@@ -155,6 +159,8 @@ def main():
         "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
         "host_wall_s_timed": round(t_host, 4),
     }
+    if ms_other is not None:
+        out["fwd_bwd_us_by_amax_algo"] = {args.algo: round(ms_per_step * 1e3, 2), other: round(ms_other * 1e3, 2)}
     if out["vs_baseline"] is not None:
         out["baseline_note"] = ("pages' H100 float8nocompile ATOMIC_MAX fwd+bwd time for this shape "
                                 "(read as microseconds), converted to TFLOP/s; another machine's number")
@@ -231,12 +237,29 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                            "gbs": round(4 * el / (ms * 1e-3) / 1e9, 1),
                            "frac_hbm_peak": round(4 * el / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "bytes_per_elem": 4}
-    ms, n, el = acc["amax"]
-    if n:
-        k["amax_" + args.algo] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
-                                  "gbs": round(2 * el / (ms * 1e-3) / 1e9, 1),
-                                  "frac_hbm_peak": round(2 * el / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                  "bytes_per_elem": 2}
+    # amax alone, both algorithms, on the step's three tensors
+    for algo in ("atomic", "twopass"):
+        tot_ms, n, el = 0.0, 0, 0
+        for t in range(args.warmup + args.steps):
+            evs = []
+            for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
+                for tensor, st in ((x, buf.sx), (w, buf.sw), (dy, buf.sdy)):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    f8lin.amax(tensor, st.amax, buf.ws, algo)
+                    b.record(stream)
+                    evs.append((a, b, tensor.numel()))
+            torch.cuda.synchronize()
+            if t >= args.warmup:
+                for a, b, units in evs:
+                    tot_ms += a.elapsed_time(b)
+                    n += 1
+                    el += units
+        k["amax_" + algo] = {"avg_us": round(tot_ms / n * 1e3, 3), "launches": n,
+                             "gbs": round(2 * el / (tot_ms * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(2 * el / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "bytes_per_elem": 2}
     return {"kernels": k}
 
 
@@ -253,19 +276,25 @@ def cpu_baseline(args, wl, sets, np, torch):
     flops = 0
     secs = 0.0
     rows_used = []
+    host = []
     for (l, x, w, dy) in sets[0]:
         ms = min(l.M, args.cpu_rows)
         rows_used.append(ms)
-        xb, wb, dyb = bits(x[:ms]), bits(w), bits(dy[:ms])
-        t0 = time.perf_counter()
-        oracle.linear_step(xb, wb, dyb, gemms=True)
-        secs += time.perf_counter() - t0
-        flops += 6 * ms * l.N * l.K
+        host.append((l, ms, bits(x[:ms]), bits(w), bits(dy[:ms])))
+    reps = 0
+    while reps < 30 and (reps == 0 or secs < 10.0):  # about 10 s of CPU work, repeated samples
+        for l, ms, xb, wb, dyb in host:
+            t0 = time.perf_counter()
+            oracle.linear_step(xb, wb, dyb, gemms=True)
+            secs += time.perf_counter() - t0
+            flops += 6 * ms * l.N * l.K
+        reps += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": round(secs, 2),
-            "sample": f"one step of {wl.name} on the first {rows_used} rows of X and dY per linear (full W): "
-                      "amax, scale, cast+transpose of X, W, dY and the three fp64 GEMM references",
+            "sample": f"{reps} repetition(s) of one step of {wl.name} on the first {rows_used} rows of X and dY "
+                      "per linear (full W): amax, scale, cast+transpose of X, W, dY and the three fp64 GEMM "
+                      "references",
             "host_cpus_visible": len(os.sched_getaffinity(0))}
 
 

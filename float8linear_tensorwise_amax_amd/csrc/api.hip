@@ -20,7 +20,7 @@
 namespace f8lin {
 namespace {
 
-constexpr int64_t kMaxDim = (int64_t)1 << 30;        // per matrix dimension
+constexpr int64_t kMaxDim = (int64_t)1 << 22;        // per matrix dimension (32-bit tile offsets)
 constexpr int64_t kMaxElems = (int64_t)1 << 40;      // per tensor
 constexpr int kUpdateBatch = 16;
 

@@ -37,9 +37,9 @@
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work on it: nothing synchronises, nothing is read back to the
  *    host, nothing is allocated, and no pointer is kept after the call.
- *  - Matrix dimensions (rows, cols, M, N, K) must be >= 0 and multiples of
- *    16 (every row is then a whole number of 16-byte vectors in both the
- *    row-major and the transposed layout).  A zero dimension is allowed and
+ *  - Matrix dimensions (rows, cols, M, N, K) must be >= 0, at most 2^22
+ *    and multiples of 16 (every row is then a whole number of 16-byte
+ *    vectors in both the row-major and the transposed layout).  A zero dimension is allowed and
  *    computes the degenerate result (e.g. dW = 0 when M = 0).
  *  - Arguments are checked before anything is launched; on error nothing is
  *    enqueued and a non-zero f8lin_status is returned.  F8LIN_EHIP reports a
@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   F8LIN_OK = 0,
   F8LIN_EINVAL = 1,     /* null pointer, bad enum, overlapping buffers, bad count */
-  F8LIN_ESHAPE = 2,     /* negative dimension, or not a multiple of 16 */
+  F8LIN_ESHAPE = 2,     /* negative dimension, above 2^22, or not a multiple of 16 */
   F8LIN_EALIGN = 3,     /* a pointer not 16-byte aligned */
   F8LIN_EWORKSPACE = 4, /* workspace missing or smaller than f8lin_workspace_bytes() */
   F8LIN_EHIP = 5        /* a HIP launch failed */
