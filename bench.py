@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="linear4096_m4096")
-    p.add_argument("--algo", default="atomic", choices=["atomic", "twopass"])
+    p.add_argument("--algo", default="twopass", choices=["atomic", "twopass"],
+                   help="amax algorithm of the timed loop; the other one is timed right after")
     p.add_argument("--rotate", type=int, default=0, help="input sets to rotate (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4096, help="rows of X/dY in the oracle's timed sample")

@@ -7,7 +7,7 @@ seeded synthetic workloads.
 """
 import importlib
 
-__all__ = ["f8lin", "inputs"]
+__all__ = ["f8lin", "inputs", "module"]
 
 
 def __getattr__(name):

@@ -8,7 +8,9 @@
 //   twopass: the same per-workgroup reduction writes one partial per
 //            workgroup; a second launch of one workgroup reduces them.
 // Both compute max |x| exactly as the max of the 15-bit magnitude fields, so
-// both give the same bits as a plain max over |x| in any order.
+// both give the same bits as a plain max over |x| in any order.  One launch
+// may reduce two tensors (the forward's X and W) with separate workgroups,
+// slots and partials per tensor.
 //
 // HBM-bound: 2 bytes read per element.  Loads are 128-bit (8 bf16), eight in
 // flight per thread per iteration.  The grid is at most one 1024-thread
@@ -26,8 +28,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kUnroll = 8;
-constexpr int kMaxGrid = 256;  // one workgroup per CU
-static_assert(kMaxGrid <= kAmaxMaxBlocks, "partials do not fit the workspace");
+static_assert(kMaxGrid * kMaxAmaxTensors + kWsPartialsOffset <= (int)(kWorkspaceBytes / 4),
+              "partials do not fit the workspace");
 
 // Max magnitude (15-bit) over this thread's grid-stride share of x[0, n).
 __device__ __forceinline__ uint32_t thread_magmax(const uint16_t *__restrict__ x, int64_t n, int64_t gtid,
@@ -75,43 +77,71 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void amax_atomic_kernel(const uint16_t *__restrict__ x, int64_t n,
-                                                               uint32_t *ws, float *amax_out) {
-  const int64_t nthreads = (int64_t)gridDim.x * kThreads;
-  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t m = block_max(thread_magmax(x, n, gtid, nthreads));
+// One launch can reduce up to kMaxAmaxTensors tensors: workgroups
+// [first[t], first[t] + grid[t]) belong to tensor t.
+struct AmaxJob {
+  const uint16_t *x;
+  int64_t n;
+  float *out;
+  int first;
+  int grid;
+};
+struct AmaxJobs {
+  AmaxJob j[kMaxAmaxTensors];
+  int count;
+};
+
+__device__ __forceinline__ int job_of(const AmaxJobs &jobs) {
+  int t = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxAmaxTensors; ++i)
+    if (i < jobs.count && (int)blockIdx.x >= jobs.j[i].first) t = i;
+  return t;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_atomic_kernel(const AmaxJobs jobs, uint32_t *ws) {
+  const int t = job_of(jobs);
+  const AmaxJob &jb = jobs.j[t];
+  const int64_t nthreads = (int64_t)jb.grid * kThreads;
+  const int64_t gtid = (int64_t)(blockIdx.x - jb.first) * kThreads + threadIdx.x;
+  const uint32_t m = block_max(thread_magmax(jb.x, jb.n, gtid, nthreads));
   if (threadIdx.x == 0) {
-    atomicMax(&ws[0], m);
+    uint32_t *slot = ws + kWsSlotWords * t;  // [0] running max, [1] ticket
+    atomicMax(&slot[0], m);
     __threadfence();
-    const uint32_t ticket = atomicAdd(&ws[1], 1u);
-    if (ticket == gridDim.x - 1) {  // every other workgroup has folded its max in
+    const uint32_t ticket = atomicAdd(&slot[1], 1u);
+    if (ticket == (uint32_t)jb.grid - 1) {  // every other workgroup of this tensor has folded its max in
       __threadfence();
-      const uint32_t all = atomicMax(&ws[0], 0u);  // atomic read of the final max
-      amax_out[0] = __uint_as_float(all << 16);
-      atomicExch(&ws[0], 0u);
-      atomicExch(&ws[1], 0u);
+      const uint32_t all = atomicMax(&slot[0], 0u);  // atomic read of the final max
+      jb.out[0] = __uint_as_float(all << 16);
+      atomicExch(&slot[0], 0u);
+      atomicExch(&slot[1], 0u);
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint16_t *__restrict__ x, int64_t n,
-                                                                uint32_t *__restrict__ partials) {
-  const int64_t nthreads = (int64_t)gridDim.x * kThreads;
-  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t m = block_max(thread_magmax(x, n, gtid, nthreads));
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const AmaxJobs jobs, uint32_t *__restrict__ ws) {
+  const int t = job_of(jobs);
+  const AmaxJob &jb = jobs.j[t];
+  const int64_t nthreads = (int64_t)jb.grid * kThreads;
+  const int64_t lb = blockIdx.x - jb.first;
+  const int64_t gtid = lb * kThreads + threadIdx.x;
+  const uint32_t m = block_max(thread_magmax(jb.x, jb.n, gtid, nthreads));
+  if (threadIdx.x == 0) ws[kWsPartialsOffset + t * kMaxGrid + lb] = m;
 }
 
-// Reduces the partials and clears them, so the workspace is zero again.
-__global__ __launch_bounds__(kThreads) void amax_final_kernel(uint32_t *__restrict__ partials, int nparts,
-                                                              float *amax_out) {
+// One workgroup per tensor reduces that tensor's partials and clears them,
+// so the workspace is zero again.
+__global__ __launch_bounds__(kThreads) void amax_final_kernel(const AmaxJobs jobs, uint32_t *__restrict__ ws) {
+  const int t = blockIdx.x;
+  uint32_t *partials = ws + kWsPartialsOffset + t * kMaxGrid;
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) {
+  for (int i = threadIdx.x; i < jobs.j[t].grid; i += kThreads) {
     m = max(m, partials[i]);
     partials[i] = 0u;
   }
   m = block_max(m);
-  if (threadIdx.x == 0) amax_out[0] = __uint_as_float(m << 16);
+  if (threadIdx.x == 0) jobs.j[t].out[0] = __uint_as_float(m << 16);
 }
 
 int grid_for(int64_t n) {
@@ -125,15 +155,19 @@ int grid_for(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, uint32_t *ws,
-                       hipStream_t stream) {
-  const int grid = grid_for(n);
+hipError_t launch_amax(const AmaxTensor *ts, int count, int algo, uint32_t *ws, hipStream_t stream) {
+  AmaxJobs jobs = {};
+  jobs.count = count;
+  int total = 0;
+  for (int t = 0; t < count; ++t) {
+    jobs.j[t] = AmaxJob{ts[t].x, ts[t].n, ts[t].out, total, grid_for(ts[t].n)};
+    total += jobs.j[t].grid;
+  }
   if (algo == F8LIN_AMAX_ATOMIC) {
-    amax_atomic_kernel<<<grid, kThreads, 0, stream>>>(x, n, ws, amax_out);
+    amax_atomic_kernel<<<total, kThreads, 0, stream>>>(jobs, ws);
   } else {
-    uint32_t *partials = ws + kWsPartialsOffset;
-    amax_partial_kernel<<<grid, kThreads, 0, stream>>>(x, n, partials);
-    amax_final_kernel<<<1, kThreads, 0, stream>>>(partials, grid, amax_out);
+    amax_partial_kernel<<<total, kThreads, 0, stream>>>(jobs, ws);
+    amax_final_kernel<<<count, kThreads, 0, stream>>>(jobs, ws);
   }
   return hipGetLastError();
 }

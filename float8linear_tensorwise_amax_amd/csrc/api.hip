@@ -3,7 +3,8 @@
 // here synchronises, reads device memory, or allocates.
 //
 // Forward / backward orchestration follows the layer's definition:
-//   forward : [amax X] [amax W] cast X -> X8, X8^T; cast W -> W8, W8^T;
+//   forward : [amax X, W] (one launch); cast X -> X8, X8^T and W -> W8, W8^T
+//             (one launch when both tensors share a scaling mode);
 //             Y = X8 . W8^T / (s_x s_w)
 //   backward: [amax dY] cast dY -> dY8, dY8^T (e5m2);
 //             dX = dY8 . (W8^T)^T / (s_dy s_w); dW = dY8^T . (X8^T)^T / (s_dy s_x)
@@ -159,13 +160,15 @@ int f8lin_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, void *ws
   const Range outs[2] = {{amax_out, 4}, {ws, (int64_t)kWorkspaceBytes}};
   const Range ins[1] = {{x, 2 * n}};
   if (any_overlap(outs, 2, ins, 1)) return F8LIN_EINVAL;
-  return status_of(launch_amax(x, n, algo, amax_out, (uint32_t *)ws, (hipStream_t)stream));
+  const AmaxTensor t = {x, n, amax_out};
+  return status_of(launch_amax(&t, 1, algo, (uint32_t *)ws, (hipStream_t)stream));
 }
 
 int f8lin_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
                          const f8lin_state *st, uint8_t *q, uint8_t *qt, void *stream) {
   F8_TRY(validate_cast(x, rows, cols, fmt, mode, st, q, qt));
-  return status_of(launch_cast_transpose(x, rows, cols, fmt, mode, *st, q, qt, (hipStream_t)stream));
+  const CastTensor t = {x, rows, cols, st, q, qt};
+  return status_of(launch_cast(&t, 1, fmt, mode, (hipStream_t)stream));
 }
 
 int f8lin_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, void *stream) {
@@ -215,10 +218,22 @@ int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
-  if (a.mode_x == F8LIN_DYNAMIC) F8_TRY(status_of(launch_amax(a.x, mk, a.algo, a.sx.amax, ws, s)));
-  if (a.mode_w == F8LIN_DYNAMIC) F8_TRY(status_of(launch_amax(a.w, nk, a.algo, a.sw.amax, ws, s)));
-  F8_TRY(status_of(launch_cast_transpose(a.x, a.M, a.K, F8LIN_E4M3, a.mode_x, a.sx, a.x8, a.x8t, s)));
-  F8_TRY(status_of(launch_cast_transpose(a.w, a.N, a.K, F8LIN_E4M3, a.mode_w, a.sw, a.w8, a.w8t, s)));
+  // One amax launch for every dynamic-mode tensor, one cast launch for both
+  // tensors when they share a scaling mode.
+  AmaxTensor am[2];
+  int na = 0;
+  if (a.mode_x == F8LIN_DYNAMIC) am[na++] = AmaxTensor{a.x, mk, a.sx.amax};
+  if (a.mode_w == F8LIN_DYNAMIC) am[na++] = AmaxTensor{a.w, nk, a.sw.amax};
+  if (na > 0) F8_TRY(status_of(launch_amax(am, na, a.algo, ws, s)));
+  const CastTensor cx = {a.x, a.M, a.K, &a.sx, a.x8, a.x8t};
+  const CastTensor cw = {a.w, a.N, a.K, &a.sw, a.w8, a.w8t};
+  if (a.mode_x == a.mode_w) {
+    const CastTensor both[2] = {cx, cw};
+    F8_TRY(status_of(launch_cast(both, 2, F8LIN_E4M3, a.mode_x, s)));
+  } else {
+    F8_TRY(status_of(launch_cast(&cx, 1, F8LIN_E4M3, a.mode_x, s)));
+    F8_TRY(status_of(launch_cast(&cw, 1, F8LIN_E4M3, a.mode_w, s)));
+  }
   return status_of(
       launch_gemm(a.x8, F8LIN_E4M3, a.w8, F8LIN_E4M3, a.M, a.N, a.K, a.sx.scale + 1, a.sw.scale + 1, a.y, s));
 }
@@ -251,8 +266,12 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
-  if (a.mode_dy == F8LIN_DYNAMIC) F8_TRY(status_of(launch_amax(a.dy, mn, a.algo, a.sdy.amax, ws, s)));
-  F8_TRY(status_of(launch_cast_transpose(a.dy, a.M, a.N, F8LIN_E5M2, a.mode_dy, a.sdy, a.dy8, a.dy8t, s)));
+  if (a.mode_dy == F8LIN_DYNAMIC) {
+    const AmaxTensor t = {a.dy, mn, a.sdy.amax};
+    F8_TRY(status_of(launch_amax(&t, 1, a.algo, ws, s)));
+  }
+  const CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
+  F8_TRY(status_of(launch_cast(&cdy, 1, F8LIN_E5M2, a.mode_dy, s)));
   // dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N.
   F8_TRY(status_of(launch_gemm(a.dy8, F8LIN_E5M2, a.w8t, F8LIN_E4M3, a.M, a.K, a.N, a.sdy.scale + 1,
                                a.sw.scale + 1, a.dx, s)));

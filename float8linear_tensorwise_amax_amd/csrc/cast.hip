@@ -9,7 +9,7 @@
 // no extra launch and no host round trip sit between amax and cast.
 //
 // Work decomposition (gfx950, wave64): one workgroup of 256 threads per
-// 128 x 128 tile.
+// 128 x 128 tile; one launch may cast two tensors (the forward's X and W).
 //   load   : thread t reads 16 consecutive bf16 (two 128-bit loads) of rows
 //            t/8 + 32p, p = 0..3; eight threads cover one 256-byte row segment.
 //   q      : the 16 codes go out as one 128-bit store (a 128-byte row segment
@@ -55,35 +55,57 @@ __device__ __forceinline__ void transpose4x4(const uint32_t d0, const uint32_t d
   e3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);                 // d0.3 d1.3 d2.3 d3.3
 }
 
+// Up to two tensors per launch (the forward casts X and W together):
+// workgroups [first[i], first[i] + tiles[i]) take tensor i's tiles.
+struct CastJob {
+  const uint16_t *x;
+  int64_t rows, cols;
+  const float *amax_in;   // dynamic: this tensor's amax
+  const float *history;   // delayed: its amax history
+  float *amax_acc;        // delayed: where this step's amax accumulates
+  float *scale_out;       // {scale, 1/scale}
+  uint8_t *q, *qt;
+  int tiles_x;
+  int first;
+};
+struct CastJobs {
+  CastJob j[2];
+  int count;
+};
+
 template <int FMT, int MODE, bool WRITE_T>
-__global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, const float *__restrict__ amax_in,
-    const float *__restrict__ history, float *amax_acc, float *scale_out, uint8_t *__restrict__ q,
-    uint8_t *__restrict__ qt, int tiles_x) {
+__global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs jobs) {
   __shared__ uint32_t tile[kTile * kTile / 4];
   __shared__ uint32_t red[kThreads / 64];
   constexpr float fm = fmt_max<FMT>();
+  const int job = (jobs.count > 1 && (int)blockIdx.x >= jobs.j[1].first) ? 1 : 0;
+  const CastJob &jb = jobs.j[job];
+  const uint16_t *__restrict__ x = jb.x;
+  const int64_t rows = jb.rows, cols = jb.cols;
+  uint8_t *__restrict__ q = jb.q;
+  uint8_t *__restrict__ qt = jb.qt;
+  const int local = (int)blockIdx.x - jb.first;
 
   float a;
   if constexpr (MODE == F8LIN_DYNAMIC) {
-    a = amax_in[0];
+    a = jb.amax_in[0];
   } else {
     a = 0.0f;
 #pragma unroll
     for (int i = 0; i < kHistLen; ++i) {
-      const float h = history[i];
+      const float h = jb.history[i];
       a = (h != h || a != a) ? __builtin_nanf("") : fmaxf(a, h);
     }
   }
   const float s = scale_from_amax(a, fm);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    scale_out[0] = s;
-    scale_out[1] = 1.0f / s;
+  if (local == 0 && threadIdx.x == 0) {
+    jb.scale_out[0] = s;
+    jb.scale_out[1] = 1.0f / s;
   }
 
   const int t = threadIdx.x;
-  const int64_t row0 = (int64_t)(blockIdx.x / tiles_x) * kTile;
-  const int64_t col0 = (int64_t)(blockIdx.x % tiles_x) * kTile;
+  const int64_t row0 = (int64_t)(local / jb.tiles_x) * kTile;
+  const int64_t col0 = (int64_t)(local % jb.tiles_x) * kTile;
   const int c16 = t & 7;
   const int rsub = t >> 3;
   const int64_t gcol = col0 + c16 * 16;
@@ -141,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
       uint32_t m = red[0];
 #pragma unroll
       for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
-      atomicMax(reinterpret_cast<uint32_t *>(amax_acc), m << 16);
+      atomicMax(reinterpret_cast<uint32_t *>(jb.amax_acc), m << 16);
     }
   }
 
@@ -185,32 +207,41 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const float *__restr
 }
 
 template <int FMT, int MODE>
-void launch_ct(unsigned grid, int tiles_x, const uint16_t *x, int64_t rows, int64_t cols, const f8lin_state &st,
-               uint8_t *q, uint8_t *qt, hipStream_t stream) {
-  if (qt)
-    cast_transpose_kernel<FMT, MODE, true><<<grid, kThreads, 0, stream>>>(x, rows, cols, st.amax, st.history,
-                                                                           st.amax, st.scale, q, qt, tiles_x);
+void launch_ct(unsigned grid, const CastJobs &jobs, bool write_t, hipStream_t stream) {
+  if (write_t)
+    cast_transpose_kernel<FMT, MODE, true><<<grid, kThreads, 0, stream>>>(jobs);
   else
-    cast_transpose_kernel<FMT, MODE, false><<<grid, kThreads, 0, stream>>>(x, rows, cols, st.amax, st.history,
-                                                                            st.amax, st.scale, q, qt, tiles_x);
+    cast_transpose_kernel<FMT, MODE, false><<<grid, kThreads, 0, stream>>>(jobs);
 }
 
 }  // namespace
 
-hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
-                                 const f8lin_state &st, uint8_t *q, uint8_t *qt, hipStream_t stream) {
-  // At least one workgroup even for an empty tensor: it still publishes the scale.
-  // (The C-ABI layer bounds rows * cols, so the tile count fits a 1-D grid.)
-  const int64_t gx = cols > 0 ? (cols + kTile - 1) / kTile : 1;
-  const int64_t gy = rows > 0 ? (rows + kTile - 1) / kTile : 1;
-  const unsigned grid = (unsigned)(gx * gy);
-  const int tx = (int)gx;
+hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream) {
+  // Every tensor gets at least one workgroup, even when empty: it still
+  // publishes the scale.  (The C-ABI layer bounds rows * cols, so the tile
+  // count fits a 1-D grid.)  The transposed copy is written for all tensors
+  // of a launch or for none.
+  CastJobs jobs = {};
+  jobs.count = count;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const CastTensor &t = ts[i];
+    const int64_t gx = t.cols > 0 ? (t.cols + kTile - 1) / kTile : 1;
+    const int64_t gy = t.rows > 0 ? (t.rows + kTile - 1) / kTile : 1;
+    jobs.j[i] = CastJob{t.x, t.rows, t.cols, t.st->amax, t.st->history, t.st->amax, t.st->scale, t.q, t.qt,
+                        (int)gx, (int)total};
+    total += gx * gy;
+  }
+  // (An empty tensor may pass a null qt; its workgroup writes no rows.)
+  bool write_t = false;
+  for (int i = 0; i < count; ++i) write_t = write_t || ts[i].qt != nullptr;
+  const unsigned grid = (unsigned)total;
   if (fmt == F8LIN_E4M3) {
-    if (mode == F8LIN_DYNAMIC) launch_ct<0, F8LIN_DYNAMIC>(grid, tx, x, rows, cols, st, q, qt, stream);
-    else launch_ct<0, F8LIN_DELAYED>(grid, tx, x, rows, cols, st, q, qt, stream);
+    if (mode == F8LIN_DYNAMIC) launch_ct<0, F8LIN_DYNAMIC>(grid, jobs, write_t, stream);
+    else launch_ct<0, F8LIN_DELAYED>(grid, jobs, write_t, stream);
   } else {
-    if (mode == F8LIN_DYNAMIC) launch_ct<1, F8LIN_DYNAMIC>(grid, tx, x, rows, cols, st, q, qt, stream);
-    else launch_ct<1, F8LIN_DELAYED>(grid, tx, x, rows, cols, st, q, qt, stream);
+    if (mode == F8LIN_DYNAMIC) launch_ct<1, F8LIN_DYNAMIC>(grid, jobs, write_t, stream);
+    else launch_ct<1, F8LIN_DELAYED>(grid, jobs, write_t, stream);
   }
   return hipGetLastError();
 }

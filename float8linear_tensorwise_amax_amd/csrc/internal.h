@@ -9,18 +9,30 @@
 
 namespace f8lin {
 
-// Workspace layout (uint32 words): [0] atomic-max accumulator, [1] ticket,
-// [64, 64 + kAmaxMaxBlocks) two-pass partial maxima.
-constexpr int kAmaxMaxBlocks = 1024;
+// Workspace layout (uint32 words): for tensor t of a launch, words
+// [kWsSlotWords*t, +2) hold the atomic variant's running max and ticket;
+// words [kWsPartialsOffset + kMaxGrid*t, +kMaxGrid) the two-pass partials.
+constexpr int kMaxAmaxTensors = 2;
+constexpr int kMaxGrid = 256;  // amax workgroups per tensor: one per CU
+constexpr int kWsSlotWords = 32;
 constexpr int kWsPartialsOffset = 64;
 constexpr size_t kWorkspaceBytes = 8192;
-static_assert((kWsPartialsOffset + kAmaxMaxBlocks) * 4 <= kWorkspaceBytes, "workspace too small");
 
-hipError_t launch_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, uint32_t *ws,
-                       hipStream_t stream);
+struct AmaxTensor {
+  const uint16_t *x;
+  int64_t n;
+  float *out;
+};
+hipError_t launch_amax(const AmaxTensor *ts, int count, int algo, uint32_t *ws, hipStream_t stream);
 
-hipError_t launch_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
-                                 const f8lin_state &st, uint8_t *q, uint8_t *qt, hipStream_t stream);
+// Up to two casts (same format and scaling mode) in one launch.
+struct CastTensor {
+  const uint16_t *x;
+  int64_t rows, cols;
+  const f8lin_state *st;
+  uint8_t *q, *qt;
+};
+hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream);
 
 hipError_t launch_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, hipStream_t stream);
 

@@ -139,6 +139,19 @@ class ScalingState:
             getattr(self, k).copy_(sd[k])
 
 
+class ScaleView:
+    """A state that only carries {scale, 1/scale} (what backward reads of the
+    forward's X and W states), e.g. a snapshot taken at forward time."""
+
+    def __init__(self, scale: torch.Tensor):
+        if scale.numel() != 2 or scale.dtype != torch.float32 or not scale.is_contiguous():
+            raise ValueError("ScaleView needs a contiguous float32 tensor of 2 elements")
+        self.scale = scale
+
+    def c_struct(self) -> State:
+        return State(None, self.scale.data_ptr(), None, None)
+
+
 # ----------------------------------------------------------------- entry points
 
 def amax(x: torch.Tensor, out: torch.Tensor, ws: torch.Tensor, algo="atomic", stream=None):
