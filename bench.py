@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4096, help="rows of X/dY in the oracle's timed sample")
     p.add_argument("--only-timed", action="store_true", help="skip the instrumented pass (for profiling)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes three times (counter calibration)")
     return p.parse_args()
 
 
@@ -88,6 +90,19 @@ def main():
     import numpy as np
     import torch
     from float8linear_tensorwise_amax_amd import f8lin, inputs
+
+    if args.calibrate_copy:
+        # A plain copy of known size: HBM counters of the same profiler run,
+        # divided by these bytes, give the counters' scale factors.
+        n = args.calibrate_copy
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
 
     wl = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
