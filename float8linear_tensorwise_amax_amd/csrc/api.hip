@@ -272,12 +272,12 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
   }
   const CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
   F8_TRY(status_of(launch_cast(&cdy, 1, F8LIN_E5M2, a.mode_dy, s)));
-  // dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N.
-  F8_TRY(status_of(launch_gemm(a.dy8, F8LIN_E5M2, a.w8t, F8LIN_E4M3, a.M, a.K, a.N, a.sdy.scale + 1,
-                               a.sw.scale + 1, a.dx, s)));
-  // dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
-  return status_of(launch_gemm(a.dy8t, F8LIN_E5M2, a.x8t, F8LIN_E4M3, a.N, a.K, a.M, a.sdy.scale + 1,
-                               a.sx.scale + 1, a.dw, s));
+  // One launch for both GEMMs:
+  //   dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N;
+  //   dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
+  const GemmDesc g[2] = {{a.dy8, a.w8t, a.sdy.scale + 1, a.sw.scale + 1, a.dx, a.M, a.K, a.N},
+                         {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
+  return status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s));
 }
 
 int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream) {

@@ -4,6 +4,8 @@
 //   C (M, N) bf16 = (A (M, K) . B (N, K)^T) * inv_a * inv_b
 // Both operands are K-contiguous ("TN"); the cast kernel writes the
 // transposed fp8 copies so that forward, dgrad and wgrad all take this form.
+// One launch runs a list of up to two such problems (the backward's dgrad
+// and wgrad go together).
 //
 // gfx950 design (each choice measured on MI355X):
 //   * v_mfma_f32_32x32x64_f8f6f4 (the scaled builtin with zero scale operands
@@ -11,27 +13,45 @@
 //     cbsz / blgp.  A lane feeds the same 32 K-bytes of its A row and of its
 //     B row, so A and B share one K order and the instruction's internal K
 //     order cannot matter.
-//   * Two waves per SIMD: one wave per SIMD reached only ~75-85% of the MFMA
-//     rate in an issue-rate probe, two waves ~97%.  Workgroups:
+//   * Two waves per SIMD (an issue-rate probe: one wave per SIMD reached
+//     ~75-85% of the MFMA rate, two waves ~97%).  Workgroups:
 //       big   256 x 256 tile, 8 waves (2 x 4), wave tile 128 x 64
 //             (128 fp32 accumulators per lane), one workgroup per CU;
 //       small 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64, two per CU,
-//             for shapes with too few big tiles to fill 256 CUs.
-//   * K step of 128 bytes, two LDS stages.  Global -> LDS copies use
+//             for problems with too few big tiles to fill 256 CUs.
+//   * K block of 128 bytes in two LDS stages.  Global -> LDS copies use
 //     buffer_load_dwordx4 ... lds (no register staging); eight lanes fetch
-//     one 128-byte row line.  The buffer resource's range check returns
-//     zeros for rows past M / N, and K chunks past K are pointed outside the
-//     range, so ragged edges load zeros with no branches.
+//     one full 128-byte row line (64-byte row segments, i.e. K blocks of 64,
+//     loaded ~1.5x slower).  The buffer resource's range check returns zeros
+//     for rows past M / N, and K chunks past K point outside the range, so
+//     ragged edges load zeros with no branches.
 //   * LDS slot of (row r, 16-byte chunk c) = r*8 + (c ^ ((r>>1) & 7)): every
 //     16 consecutive rows at one chunk fall in 16 distinct bank groups, so
 //     the 128-bit fragment reads are conflict-free.
-//   * Fragments are refilled in place right after their last use, so the
-//     next sub-step's LDS reads overlap the current MFMAs with one register
-//     set; one barrier per K step, placed after the first row of MFMAs of the
-//     second sub-step, both publishes stage k+1 and retires stage k.
-//   * Epilogue: fp32 accumulator * (inv_a * inv_b) rounded once to bf16
-//     (nearest even), staged through LDS per wave and written as 16-byte
-//     row segments.
+//   * Schedule (fixed with scheduling fences, since the compiler otherwise
+//     clusters the LDS reads after the MFMAs and the waves stall on them):
+//     MFMAs go column by column over the wave tile; each fragment register is
+//     refilled from LDS right after its last MFMA, at least three MFMAs before
+//     its next use.  One barrier per K block sits after the first column of
+//     its second half: it publishes block k+1 (each wave first waits for its
+//     own copies) and retires block k, whose buffer then receives block k+2;
+//     those copies are spread between the MFMAs that follow.
+//   * The matrix cores and the memory system together exceed the chip's power
+//     budget: the shader clock drops from 2.4 GHz to ~1.7-2.0 GHz while this
+//     loop runs (read with s_memtime against the constant-rate counter), so
+//     bytes moved per flop cost time even when they are hidden.
+//   * Persistent workgroups walk an XCD-aware tile list.  Workgroup b runs on
+//     XCD b % 8 (round-robin dispatch), and each XCD has its own L2, so XCD x
+//     owns a contiguous range of the tile list, laid out in groups of G
+//     tile-rows walked column by column: the tiles an XCD runs at once form a
+//     compact patch whose A and B slices its L2 shares (4096^3: 96 MiB read
+//     past L2 instead of 144 MiB with row-major order).  A workgroup's output
+//     stores drain while its next tile's loads and MFMAs run.
+//   * Epilogue: acc * (inv_a * inv_b) in fp32, then two adjacent columns are
+//     brought into one lane with a DPP swap and rounded to a bf16 pair by
+//     v_cvt_pk_bf16_f32 (nearest even; checked against a software rounding on
+//     all 2^32 binary32 patterns), staged through LDS per wave and written as
+//     16-byte row segments.
 #include "device_common.h"
 #include "internal.h"
 
@@ -39,236 +59,317 @@ namespace f8lin {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
+constexpr int kXcds = 8;
+constexpr int kCUs = 256;
 // Every matrix dimension is at most 2^22 (checked at the C ABI), so a tile's
 // byte range rows * K stays below 2^31 and this offset is always outside it.
 constexpr int kOutOfRange = (int)0x80000000u;
 
+struct Problem {
+  const uint8_t *a, *b;
+  const float *inv_a, *inv_b;
+  uint16_t *c;
+  int M, N, K;
+  int tiles_m, tiles_n, first;  // first: index of this problem's first tile in the list
+};
+struct Batch {
+  Problem p[kMaxGemms];
+  int count, tiles;
+};
+
 __device__ __forceinline__ int slot128(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-__device__ __forceinline__ void wait_vmcnt0() {
-  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their no-wait maxima
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-// Tile of workgroup b.  Workgroups are dispatched round-robin over the 8
-// XCDs (b -> XCD b % 8), and each XCD has its own L2, so XCD x is given the
-// contiguous tile range [x*T/8, (x+1)*T/8), walked in groups of G tile-rows,
-// column by column: the tiles an XCD runs at once form a compact patch
-// (G tile-rows x a few tile-columns) whose A and B slices its L2 shares.
-// With row-major order an XCD's concurrent tiles spanned many tile-rows and
-// each XCD re-fetched them (measured: 4.5x the operand bytes past L2).
+// (tile-row, tile-column) of a problem's local tile index: groups of G
+// tile-rows, each walked column by column.
 template <int G>
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int T = tiles_m * tiles_n;
-  const int per = T / 8;
-  int t = b;
-  if (b < per * 8) t = (b % 8) * per + b / 8;
+__device__ __forceinline__ void tile_coords(int local, int tiles_m, int tiles_n, int &tm, int &tn) {
   const int gsize = G * tiles_n;
-  const int grp = t / gsize, in = t % gsize;
+  const int grp = local / gsize, in = local % gsize;
   const int gm = min(G, tiles_m - grp * G);
   tm = grp * G + in % gm;
   tn = in / gm;
 }
 
-template <int FA, int FB, int BM, int BN, int WAVES_M, int WAVES_N, int MIN_BLOCKS, int G>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MIN_BLOCKS) void gemm_fp8_tn_kernel(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, int M, int N, int K,
-    const float *__restrict__ inv_a, const float *__restrict__ inv_b, uint16_t *__restrict__ C, int tiles_m,
-    int tiles_n) {
-  constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
-  constexpr int TM = WTM / 32, TN = WTN / 32;            // 32x32 MFMA tiles per wave
-  constexpr int OPA = BM * kBK, OPB = BN * kBK;          // bytes per operand per stage
+template <bool B>
+using bool_t = std::integral_constant<bool, B>;
+
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const Batch batch) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
+  constexpr int OPA = BM * kBK, OPB = BN * kBK;  // bytes per operand per stage
   constexpr int STB = OPA + OPB;
-  constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);  // 1 KB copies per wave per stage
-  static_assert(LA >= 1 && LB >= 1 && TM >= 2 && TN >= 1, "tile configuration");
-  static_assert(NW * WTM * WTN * 2 <= 2 * STB, "epilogue staging must fit in LDS");
+  constexpr int LA = OPA / 1024 / NW, LB = OPB / 1024 / NW;  // 1 KB copies per wave per stage
+  constexpr int LQ = LA + LB;
+  constexpr int RB = WTN * 2;  // bytes per staged output row
+  static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 2, "tile configuration");
+  static_assert(LQ <= 15, "vmcnt immediate");
+  static_assert(NW * WTM * RB <= 2 * STB, "epilogue staging must fit in LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int tm, tn;
-  tile_of<G>((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t rsa =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(A + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(B + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+  const int g = lane >> 5;  // K half within a 64-byte sub-step
+  const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
 
-  // Global offset (without the K step base) and K byte of each 16-byte slot
-  // this lane copies: slot s = (wave * L + j) * 64 + lane.
-  int offa[LA], kca[LA], offb[LB], kcb[LB];
-#pragma unroll
-  for (int j = 0; j < LA; ++j) {
-    const int s = (wave * LA + j) * 64 + lane;
-    const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-    offa[j] = r * K + c * 16;
-    kca[j] = c * 16;
-  }
-#pragma unroll
-  for (int j = 0; j < LB; ++j) {
-    const int s = (wave * LB + j) * 64 + lane;
-    const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-    offb[j] = r * K + c * 16;
-    kcb[j] = c * 16;
-  }
-  auto issue = [&](int kt) {
-    const int k0 = kt * kBK;
-    uint8_t *stage = smem + (kt & 1) * STB;
+  // This workgroup's share of the tile list: XCD x owns [start, start + len)
+  // and its wx workgroups take every wx-th tile of it.
+  const int xcd = (int)blockIdx.x % kXcds, local_wg = (int)blockIdx.x / kXcds;
+  const int nwg = (int)gridDim.x;
+  const int per = batch.tiles / kXcds, rem = batch.tiles % kXcds;
+  const int start = xcd * per + min(xcd, rem), len = per + (xcd < rem ? 1 : 0);
+  const int wx = nwg / kXcds + (xcd < nwg % kXcds ? 1 : 0);
+
+  for (int it = local_wg; it < len; it += wx) {
+    const int t = start + it;
+    const int pi = (batch.count > 1 && t >= batch.p[1].first) ? 1 : 0;
+    const Problem P = batch.p[pi];
+    const int M = P.M, N = P.N, K = P.K;
+    int tm, tn;
+    tile_coords<G>(t - P.first, P.tiles_m, P.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t rsa =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(P.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(P.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+
+    // Global offset (without the K block base) and K byte of each 16-byte
+    // slot this lane copies: A slot s = (wave * LA + j) * 64 + lane, same for B.
+    int offa[LA], kca[LA], offb[LB], kcb[LB];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-      const int vo = (kca[j] + k0 < K) ? offa[j] + k0 : kOutOfRange;  // past K: outside the range -> 0
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)(stage + (wave * LA + j) * 1024), 16, vo, 0, 0, 0);
+      const int s = (wave * LA + j) * 64 + lane;
+      const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+      offa[j] = r * K + c * 16;
+      kca[j] = c * 16;
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-      const int vo = (kcb[j] + k0 < K) ? offb[j] + k0 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(stage + OPA + (wave * LB + j) * 1024), 16, vo, 0,
-                                               0, 0);
+      const int s = (wave * LB + j) * 64 + lane;
+      const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+      offb[j] = r * K + c * 16;
+      kcb[j] = c * 16;
     }
-  };
-
-  const int wm = (wave / WAVES_N) * WTM, wn = (wave % WAVES_N) * WTN;
-  const int g = lane >> 5;  // K half within a 64-byte sub-step
-  int arow[TM], brow[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) arow[i] = wm + i * 32 + (lane & 31);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) brow[j] = wn + j * 32 + (lane & 31);
-
-  v16f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // Fragment of row r for sub-step ks (0/1) of the K step in `stage`:
-  // chunks ks*4 + g*2 and +1 (32 K-bytes).
-  auto rd = [&](int stage, int op_off, int r, int ks) {
-    const u32x4 *st = (const u32x4 *)(smem + stage * STB + op_off);
-    const int c = ks * 4 + g * 2;
-    const u32x4 lo = st[slot128(r, c)], hi = st[slot128(r, c + 1)];
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  };
-  auto mfma = [&](const v8i &a, const v8i &b, v16f &c) {
-    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
-  };
-
-  v8i fa[TM], fb[TN];
-  const int nk = (K + kBK - 1) / kBK;
-  if (nk > 0) {
-    issue(0);
-    wait_vmcnt0();
-    __builtin_amdgcn_s_barrier();
-    if (nk > 1) issue(1);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = rd(0, 0, arow[i], 0);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = rd(0, OPA, brow[j], 0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    // sub-step 0: fragments hold (kt, 0); refill with (kt, 1)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        mfma(fa[i], fb[j], acc[i][j]);
-        if (i == TM - 1) fb[j] = rd(cur, OPA, brow[j], 1);
+    // copy q (0 .. LQ-1) of K block kt into stage kt & 1
+    auto issue_one = [&](int kt, int q) {
+      const int k0 = kt * kBK;
+      uint8_t *stage = smem + (kt & 1) * STB;
+      if (q < LA) {
+        const int vo = (kca[q] + k0 < K) ? offa[q] + k0 : kOutOfRange;  // past K: outside the range -> 0
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)(stage + (wave * LA + q) * 1024), 16, vo, 0, 0, 0);
+      } else {
+        const int j = q - LA;
+        const int vo = (kcb[j] + k0 < K) ? offb[j] + k0 : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(stage + OPA + (wave * LB + j) * 1024), 16, vo, 0,
+                                                 0, 0);
       }
-      fa[i] = rd(cur, 0, arow[i], 1);
-    }
-    // sub-step 1: after its first row, stage kt+1 is resident (every wave waited
-    // for its own copies, then the barrier) and every wave is done with stage
-    // kt, whose buffer then receives stage kt+2.
+    };
+
+    int arow[TM], brow[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) mfma(fa[0], fb[j], acc[0][j]);
-    if (more) {
-      wait_vmcnt0();
+    for (int i = 0; i < TM; ++i) arow[i] = wm + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) brow[j] = wn + j * 32 + (lane & 31);
+    // Fragment of row r for sub-step ks (0/1) of the K block in `stage`:
+    // chunks ks*4 + g*2 and +1 (32 K-bytes).
+    auto rd = [&](int stage, int op_off, int r, int ks) {
+      const u32x4 *st = (const u32x4 *)(smem + stage * STB + op_off);
+      const int c = ks * 4 + g * 2;
+      const u32x4 lo = st[slot128(r, c)], hi = st[slot128(r, c + 1)];
+      return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    v8i fa[TM], fb[TN];
+    auto mfma = [&](const v8i &a, const v8i &b, v16f &c) {
+      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+    };
+    auto col0 = [&]() {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) mfma(fa[i], fb[0], acc[i][0]);
+    };
+    // Columns 1 .. TN-1 of the current sub-step.  With REFILL, fb[j] is
+    // refilled with sub-step (stage, ks) after column j and fa[i] after its
+    // MFMA in the last column (fb[0] was refilled by the caller); with
+    // kt >= 0, the LQ copies of K block kt are spread over these MFMAs.
+    auto cols = [&](auto REFILL, int stage, int ks, int kt) {
+      constexpr int nmf = (TN - 1) * TM;
+      int q = 0, mf = 0;
+#pragma unroll
+      for (int j = 1; j < TN; ++j) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          mfma(fa[i], fb[j], acc[i][j]);
+          if constexpr (decltype(REFILL)::value) {
+            if (j == TN - 1) fa[i] = rd(stage, 0, arow[i], ks);
+          }
+          ++mf;
+          if (kt >= 0) {
+            const int upto = (mf * LQ + nmf - 1) / nmf;
+            while (q < upto) issue_one(kt, q++);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (decltype(REFILL)::value) fb[j] = rd(stage, OPA, brow[j], ks);
+      }
+    };
+    // K block s: the fragments hold its sub-step 0 and column 0 is done.
+    // NEXT: a block s+1 exists; DMA: block s+2 exists (copied during this one).
+    const int nk = (K + kBK - 1) / kBK;
+    auto block = [&](int s, auto NEXT, auto DMA) {
+      const int cb = s & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      fb[0] = rd(cb, OPA, brow[0], 1);
+      cols(bool_t<true>(), cb, 1, -1);  // rest of sub-step 0; fragments <- sub-step 1
+      __builtin_amdgcn_sched_barrier(0);
+      col0();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(NEXT)::value) {
+        // block s+1 resident (own copies, then everyone's), every read of
+        // block s done everywhere: its buffer can take block s+2
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        fb[0] = rd(cb ^ 1, OPA, brow[0], 0);
+        cols(bool_t<true>(), cb ^ 1, 0, decltype(DMA)::value ? s + 2 : -1);
+        __builtin_amdgcn_sched_barrier(0);
+        col0();
+      } else {
+        cols(bool_t<false>(), 0, 0, -1);
+      }
+    };
+
+    if (nk > 0) {
+#pragma unroll
+      for (int q = 0; q < LQ; ++q) issue_one(0, q);
+      if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < LQ; ++q) issue_one(1, q);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | LQ);  // vmcnt(LQ): block 0 resident
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      }
       __builtin_amdgcn_s_barrier();
-      if (kt + 2 < nk) issue(kt + 2);
-      fa[0] = rd(cur ^ 1, 0, arow[0], 0);
-    }
 #pragma unroll
-    for (int i = 1; i < TM; ++i) {
+      for (int j = 0; j < TN; ++j) fb[j] = rd(0, OPA, brow[j], 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = rd(0, 0, arow[i], 0);
+      col0();
+      int s = 0;
+      for (; s + 2 < nk; ++s) block(s, bool_t<true>(), bool_t<true>());
+      if (s + 1 < nk) block(s++, bool_t<true>(), bool_t<false>());
+      block(s, bool_t<false>(), bool_t<false>());
+    }
+
+    // Epilogue.  Lane (column c = lane & 31, half h = lane >> 5) holds, per
+    // 32x32 tile, rows 8*(v>>2) + 4*h + (v&3) for v = 0..15.  Even lanes take
+    // column pair (c, c+1) at even v, odd lanes (c-1, c) at odd v, exchanging
+    // the missing value with the neighbour lane; the pair is one 32-bit LDS
+    // word.  Rows of even / odd v differ in parity and rows of the two halves
+    // in bit 2 (which swaps the 64-byte halves of the row), so each write is
+    // free of bank conflicts.
+    __syncthreads();  // every wave is done with the stage buffers
+    const float alpha = P.inv_a[0] * P.inv_b[0];
+    uint8_t *wreg = smem + wave * (WTM * RB);
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        mfma(fa[i], fb[j], acc[i][j]);
-        if (i == TM - 1 && more) fb[j] = rd(cur ^ 1, OPA, brow[j], 0);
+        const int cpair = j * 32 + (lane & 30);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float ve = acc[i][j][2 * k] * alpha, vo = acc[i][j][2 * k + 1] * alpha;
+          const float send = odd ? ve : vo;
+          const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+          const f32x2 pair = odd ? f32x2{recv, vo} : f32x2{ve, recv};
+          const int v = 2 * k + (odd ? 1 : 0);
+          const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          *(bf16x2 *)(wreg + row * RB + ((cpair * 2) ^ (((row >> 2) & 1) << 6))) =
+              __builtin_convertvector(pair, bf16x2);
+        }
       }
-      if (more) fa[i] = rd(cur ^ 1, 0, arow[i], 0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    constexpr int CPR = RB / 16;  // 16-byte chunks per row
+#pragma unroll
+    for (int k = 0; k < WTM * CPR / 64; ++k) {
+      const int idx = k * 64 + lane;
+      const int row = idx / CPR, ch = idx % CPR;
+      const u32x4 v = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ (((row >> 2) & 1) << 6)));
+      const int grow = m0 + wm + row, gcol = n0 + wn + ch * 8;
+      if (grow < M && gcol < N) *(u32x4 *)(P.c + (int64_t)grow * N + gcol) = v;
     }
-  }
-
-  // Epilogue: each wave stages its WTM x WTN bf16 tile in its own LDS region
-  // (rows of WTN*2 bytes, 64-byte halves swapped on rows with bit 2 set to
-  // spread the two row groups of a store over different banks), then writes
-  // 16-byte row segments.
-  __syncthreads();
-  constexpr int RB = WTN * 2;
-  const float alpha = inv_a[0] * inv_b[0];
-  uint8_t *wreg = smem + wave * (WTM * RB);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = j * 32 + (lane & 31);
-        *(uint16_t *)(wreg + row * RB + ((col * 2) ^ (((row >> 2) & 1) << 6))) =
-            (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
-      }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-  __builtin_amdgcn_wave_barrier();
-  constexpr int CPR = RB / 16;  // 16-byte chunks per row
-#pragma unroll
-  for (int it = 0; it < WTM * CPR / 64; ++it) {
-    const int idx = it * 64 + lane;
-    const int row = idx / CPR, ch = idx % CPR;
-    const u32x4 v = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ (((row >> 2) & 1) << 6)));
-    const int grow = m0 + wm + row, gcol = n0 + wn + ch * 8;
-    if (grow < M && gcol < N) *(u32x4 *)(C + (int64_t)grow * N + gcol) = v;
+    __syncthreads();  // staging reads done before the next tile's copies land
   }
 }
 
 template <int FA, int FB>
-void launch_fmt(const uint8_t *a, const uint8_t *b, int M, int N, int K, const float *ia, const float *ib,
-                uint16_t *c, hipStream_t stream) {
-  constexpr int kCUs = 256;
-  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= kCUs) {
-    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
-    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4>
-        <<<(unsigned)big, 512, 0, stream>>>(a, b, M, N, K, ia, ib, c, tiles_m, tiles_n);
+void launch_fmt(Batch &b, hipStream_t stream) {
+  int64_t big = 0;
+  for (int i = 0; i < b.count; ++i) big += (int64_t)((b.p[i].M + 255) / 256) * ((b.p[i].N + 255) / 256);
+  const bool use_big = big >= kCUs;
+  const int bm = use_big ? 256 : 128;
+  int tiles = 0;
+  for (int i = 0; i < b.count; ++i) {
+    Problem &p = b.p[i];
+    p.tiles_m = (p.M + bm - 1) / bm;
+    p.tiles_n = (p.N + bm - 1) / bm;
+    p.first = tiles;
+    tiles += p.tiles_m * p.tiles_n;
+  }
+  b.tiles = tiles;
+  if (tiles == 0) return;
+  if (use_big) {
+    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(b);
   } else {
-    const int tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
-    const int64_t small = (int64_t)tiles_m * tiles_n;
-    gemm_fp8_tn_kernel<FA, FB, 128, 128, 2, 2, 2, 8>
-        <<<(unsigned)small, 256, 0, stream>>>(a, b, M, N, K, ia, ib, c, tiles_m, tiles_n);
+    gemm_fp8_tn_kernel<FA, FB, 128, 128, 2, 2, 2, 8><<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(b);
   }
 }
 
 }  // namespace
 
+hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream) {
+  Batch b{};
+  for (int i = 0; i < count; ++i) {
+    if (d[i].M == 0 || d[i].N == 0) continue;
+    Problem &p = b.p[b.count++];
+    p.a = d[i].a;
+    p.b = d[i].b;
+    p.inv_a = d[i].inv_a;
+    p.inv_b = d[i].inv_b;
+    p.c = d[i].c;
+    p.M = (int)d[i].M;
+    p.N = (int)d[i].N;
+    p.K = (int)d[i].K;
+  }
+  if (b.count == 0) return hipSuccess;
+  if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E4M3)
+    launch_fmt<0, 0>(b, stream);
+  else if (fmt_a == F8LIN_E5M2 && fmt_b == F8LIN_E4M3)
+    launch_fmt<1, 0>(b, stream);
+  else if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E5M2)
+    launch_fmt<0, 1>(b, stream);
+  else
+    launch_fmt<1, 1>(b, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t M, int64_t N,
                        int64_t K, const float *inv_a, const float *inv_b, uint16_t *c, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E4M3)
-    launch_fmt<0, 0>(a, b, m, n, k, inv_a, inv_b, c, stream);
-  else if (fmt_a == F8LIN_E5M2 && fmt_b == F8LIN_E4M3)
-    launch_fmt<1, 0>(a, b, m, n, k, inv_a, inv_b, c, stream);
-  else if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E5M2)
-    launch_fmt<0, 1>(a, b, m, n, k, inv_a, inv_b, c, stream);
-  else
-    launch_fmt<1, 1>(a, b, m, n, k, inv_a, inv_b, c, stream);
-  return hipGetLastError();
+  const GemmDesc d{a, b, inv_a, inv_b, c, M, N, K};
+  return launch_gemms(&d, 1, fmt_a, fmt_b, stream);
 }
 
 }  // namespace f8lin

@@ -39,6 +39,17 @@ hipError_t launch_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, hipSt
 hipError_t launch_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t M, int64_t N,
                        int64_t K, const float *inv_a, const float *inv_b, uint16_t *c, hipStream_t stream);
 
+// Up to kMaxGemms GEMMs with the same operand formats in one persistent
+// launch (the backward's dgrad and wgrad).
+constexpr int kMaxGemms = 2;
+struct GemmDesc {
+  const uint8_t *a, *b;
+  const float *inv_a, *inv_b;
+  uint16_t *c;
+  int64_t M, N, K;
+};
+hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream);
+
 hipError_t launch_delayed_update(const f8lin_state *states, int n, hipStream_t stream);
 
 }  // namespace f8lin
