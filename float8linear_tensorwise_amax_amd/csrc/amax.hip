@@ -172,4 +172,19 @@ hipError_t launch_amax(const AmaxTensor *ts, int count, int algo, uint32_t *ws, 
   return hipGetLastError();
 }
 
+hipError_t launch_amax_partials(const AmaxTensor *ts, int count, uint32_t *ws, const uint32_t **parts, int *nparts,
+                                hipStream_t stream) {
+  AmaxJobs jobs = {};
+  jobs.count = count;
+  int total = 0;
+  for (int t = 0; t < count; ++t) {
+    jobs.j[t] = AmaxJob{ts[t].x, ts[t].n, ts[t].out, total, grid_for(ts[t].n)};
+    parts[t] = ws + kWsPartialsOffset + t * kMaxGrid;
+    nparts[t] = jobs.j[t].grid;
+    total += jobs.j[t].grid;
+  }
+  amax_partial_kernel<<<total, kThreads, 0, stream>>>(jobs, ws);
+  return hipGetLastError();
+}
+
 }  // namespace f8lin

@@ -219,14 +219,27 @@ int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
   // One amax launch for every dynamic-mode tensor, one cast launch for both
-  // tensors when they share a scaling mode.
+  // tensors when they share a scaling mode.  The two-pass amax leaves its
+  // partial maxima for the cast's prologue to reduce.
   AmaxTensor am[2];
   int na = 0;
   if (a.mode_x == F8LIN_DYNAMIC) am[na++] = AmaxTensor{a.x, mk, a.sx.amax};
   if (a.mode_w == F8LIN_DYNAMIC) am[na++] = AmaxTensor{a.w, nk, a.sw.amax};
-  if (na > 0) F8_TRY(status_of(launch_amax(am, na, a.algo, ws, s)));
-  const CastTensor cx = {a.x, a.M, a.K, &a.sx, a.x8, a.x8t};
-  const CastTensor cw = {a.w, a.N, a.K, &a.sw, a.w8, a.w8t};
+  const uint32_t *parts[2] = {nullptr, nullptr};
+  int nparts[2] = {0, 0};
+  if (na > 0) {
+    if (a.algo == F8LIN_AMAX_TWOPASS)
+      F8_TRY(status_of(launch_amax_partials(am, na, ws, parts, nparts, s)));
+    else
+      F8_TRY(status_of(launch_amax(am, na, a.algo, ws, s)));
+  }
+  CastTensor cx = {a.x, a.M, a.K, &a.sx, a.x8, a.x8t};
+  CastTensor cw = {a.w, a.N, a.K, &a.sw, a.w8, a.w8t};
+  {
+    int i = 0;
+    if (a.mode_x == F8LIN_DYNAMIC) cx.partials = parts[i], cx.npartials = nparts[i], ++i;
+    if (a.mode_w == F8LIN_DYNAMIC) cw.partials = parts[i], cw.npartials = nparts[i], ++i;
+  }
   if (a.mode_x == a.mode_w) {
     const CastTensor both[2] = {cx, cw};
     F8_TRY(status_of(launch_cast(both, 2, F8LIN_E4M3, a.mode_x, s)));
@@ -266,11 +279,14 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
+  CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
   if (a.mode_dy == F8LIN_DYNAMIC) {
     const AmaxTensor t = {a.dy, mn, a.sdy.amax};
-    F8_TRY(status_of(launch_amax(&t, 1, a.algo, ws, s)));
+    if (a.algo == F8LIN_AMAX_TWOPASS)
+      F8_TRY(status_of(launch_amax_partials(&t, 1, ws, &cdy.partials, &cdy.npartials, s)));
+    else
+      F8_TRY(status_of(launch_amax(&t, 1, a.algo, ws, s)));
   }
-  const CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
   F8_TRY(status_of(launch_cast(&cdy, 1, F8LIN_E5M2, a.mode_dy, s)));
   // One launch for both GEMMs:
   //   dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N;

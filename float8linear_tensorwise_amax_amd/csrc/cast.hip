@@ -5,8 +5,11 @@
 // Tensorwise scaling (pytorch/torchtitan PR #778 Summary: tensorwise dynamic
 // scaling; pytorch/ao issue #1297 repro: delayed scaling of input, weight and
 // grad_output).  The scale is computed in every workgroup's prologue from the
-// state (dynamic: state.amax; delayed: max of the 16-entry amax history), so
-// no extra launch and no host round trip sit between amax and cast.
+// state (dynamic: state.amax, or the per-workgroup partial maxima of the
+// two-pass amax, which each workgroup reduces itself -- the second pass of
+// that algorithm -- so it needs no launch of its own; delayed: max of the
+// 16-entry amax history), so no extra launch and no host round trip sit
+// between amax and cast.
 //
 // Work decomposition (gfx950, wave64): one workgroup of 256 threads per
 // 128 x 128 tile; one launch may cast two tensors (the forward's X and W).
@@ -33,6 +36,7 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+static_assert(kThreads / 64 == 4 && kMaxGrid <= kThreads, "partials reduction layout");
 
 __device__ __forceinline__ int lds_word(int row, int word) {
   // 32 words per row; 16-byte chunk index XOR (row / 16) % 8.
@@ -60,7 +64,9 @@ __device__ __forceinline__ void transpose4x4(const uint32_t d0, const uint32_t d
 struct CastJob {
   const uint16_t *x;
   int64_t rows, cols;
-  const float *amax_in;   // dynamic: this tensor's amax
+  float *amax;            // dynamic: this tensor's amax (written here when partials are given)
+  const uint32_t *partials;  // dynamic, two-pass: the partial magnitude maxima, or null
+  int npartials;
   const float *history;   // delayed: its amax history
   float *amax_acc;        // delayed: where this step's amax accumulates
   float *scale_out;       // {scale, 1/scale}
@@ -86,23 +92,6 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
   uint8_t *__restrict__ qt = jb.qt;
   const int local = (int)blockIdx.x - jb.first;
 
-  float a;
-  if constexpr (MODE == F8LIN_DYNAMIC) {
-    a = jb.amax_in[0];
-  } else {
-    a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kHistLen; ++i) {
-      const float h = jb.history[i];
-      a = (h != h || a != a) ? __builtin_nanf("") : fmaxf(a, h);
-    }
-  }
-  const float s = scale_from_amax(a, fm);
-  if (local == 0 && threadIdx.x == 0) {
-    jb.scale_out[0] = s;
-    jb.scale_out[1] = 1.0f / s;
-  }
-
   const int t = threadIdx.x;
   const int64_t row0 = (int64_t)(local / jb.tiles_x) * kTile;
   const int64_t col0 = (int64_t)(local % jb.tiles_x) * kTile;
@@ -123,6 +112,36 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
       in[p][0] = u32x4{0, 0, 0, 0};
       in[p][1] = u32x4{0, 0, 0, 0};
     }
+  }
+
+  // The scale (after the tile's loads are in flight).
+  float a;
+  if constexpr (MODE == F8LIN_DYNAMIC) {
+    if (jb.partials) {
+      uint32_t m = t < jb.npartials ? jb.partials[t] : 0u;  // at most kMaxGrid <= kThreads partials
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+      if ((t & 63) == 0) red[t >> 6] = m;
+      __syncthreads();
+      m = max(max(red[0], red[1]), max(red[2], red[3]));
+      a = __uint_as_float(m << 16);
+      __syncthreads();  // red is reused by the delayed-mode reduction below
+      if (local == 0 && t == 0) jb.amax[0] = a;
+    } else {
+      a = jb.amax[0];
+    }
+  } else {
+    a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kHistLen; ++i) {
+      const float h = jb.history[i];
+      a = (h != h || a != a) ? __builtin_nanf("") : fmaxf(a, h);
+    }
+  }
+  const float s = scale_from_amax(a, fm);
+  if (local == 0 && t == 0) {
+    jb.scale_out[0] = s;
+    jb.scale_out[1] = 1.0f / s;
   }
 
   uint32_t mag = 0;
@@ -228,8 +247,9 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
     const CastTensor &t = ts[i];
     const int64_t gx = t.cols > 0 ? (t.cols + kTile - 1) / kTile : 1;
     const int64_t gy = t.rows > 0 ? (t.rows + kTile - 1) / kTile : 1;
-    jobs.j[i] = CastJob{t.x, t.rows, t.cols, t.st->amax, t.st->history, t.st->amax, t.st->scale, t.q, t.qt,
-                        (int)gx, (int)total};
+    jobs.j[i] = CastJob{t.x,          t.rows,       t.cols,      t.st->amax, t.partials, t.npartials,
+                        t.st->history, t.st->amax, t.st->scale, t.q,        t.qt,       (int)gx,
+                        (int)total};
     total += gx * gy;
   }
   // (An empty tensor may pass a null qt; its workgroup writes no rows.)

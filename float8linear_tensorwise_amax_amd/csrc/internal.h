@@ -24,6 +24,11 @@ struct AmaxTensor {
   float *out;
 };
 hipError_t launch_amax(const AmaxTensor *ts, int count, int algo, uint32_t *ws, hipStream_t stream);
+// The two-pass amax's first pass alone: tensor t's partial maxima (15-bit
+// magnitudes) are left at parts[t][0 .. nparts[t]) inside the workspace, for
+// the cast to reduce in its prologue (ts[t].out is not written).
+hipError_t launch_amax_partials(const AmaxTensor *ts, int count, uint32_t *ws, const uint32_t **parts, int *nparts,
+                                hipStream_t stream);
 
 // Up to two casts (same format and scaling mode) in one launch.
 struct CastTensor {
@@ -31,6 +36,10 @@ struct CastTensor {
   int64_t rows, cols;
   const f8lin_state *st;
   uint8_t *q, *qt;
+  // dynamic mode: partial maxima of the two-pass amax to reduce (then
+  // st->amax is written), or null to read st->amax
+  const uint32_t *partials = nullptr;
+  int npartials = 0;
 };
 hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream);
 

@@ -101,7 +101,11 @@ typedef struct {
 
 /* Bytes of device workspace that f8lin_amax / f8lin_forward /
  * f8lin_backward need (a constant).  The caller zero-fills it once before
- * first use; every call leaves it zero-filled again. */
+ * first use.  Every call leaves the words that must start at zero (the
+ * atomic algorithm's running max and ticket) at zero again; f8lin_amax
+ * leaves the whole workspace zero-filled, while f8lin_forward /
+ * f8lin_backward with the two-pass algorithm leave its partial maxima in
+ * the workspace (every call overwrites them before reading them). */
 size_t f8lin_workspace_bytes(void);
 
 /* Human-readable name of a status code (static string). */
