@@ -183,9 +183,11 @@ def main():
 
     if not args.only_timed:
         out.update(instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed))
-        rl = out["kernels"]["gemm"]
+        # the step's dominant kernel: the backward's dgrad + wgrad launch
+        rl = out["kernels"]["gemm_bwd_pair"]
         traffic = load_traffic(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "csrc", "gemm.hip"))
-        out["roofline"] = {"kernel": "gemm_fp8_tn", "bound": "mfma", "achieved": rl["tflops"],
+        out["roofline"] = {"kernel": "gemm_fp8_tn_kernel<e5m2,e4m3> (dgrad + wgrad, one launch)",
+                           "bound": "mfma", "achieved": rl["tflops"],
                            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(rl["tflops"] / PEAK_FP8_TFLOPS, 4),
                            "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None)}
@@ -202,8 +204,9 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
     """Per-kernel durations: the same launch sequence as f8lin_forward /
     f8lin_backward, issued entry point by entry point with HIP events between
     the calls on the launch stream."""
-    acc = {"amax": [0.0, 0, 0.0], "cast": [0.0, 0, 0.0], "gemm": [0.0, 0, 0.0]}  # ms, launches, units
-    gemm_bytes = []
+    acc = {"amax": [0.0, 0, 0.0], "cast": [0.0, 0, 0.0], "gemm_fwd": [0.0, 0, 0.0],
+           "gemm_bwd_pair": [0.0, 0, 0.0]}  # ms, launches, units
+    gemm_bytes = {"gemm_fwd": [], "gemm_bwd_pair": []}
 
     def timed(kind, fn, units):
         a = torch.cuda.Event(enable_timing=True)
@@ -222,20 +225,22 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                 timed("amax", lambda: f8lin.amax(w, buf.sw.amax, buf.ws, args.algo), w.numel())
             timed("cast", lambda: f8lin.cast_transpose(x, "e4m3", mode, buf.sx, buf.x8, buf.x8t), x.numel())
             timed("cast", lambda: f8lin.cast_transpose(w, "e4m3", mode, buf.sw, buf.w8, buf.w8t), w.numel())
-            timed("gemm", lambda: f8lin.gemm(buf.x8, "e4m3", buf.w8, "e4m3", buf.sx.inv_scale, buf.sw.inv_scale,
-                                             buf.y), 2 * l.M * l.N * l.K)
+            timed("gemm_fwd", lambda: f8lin.gemm(buf.x8, "e4m3", buf.w8, "e4m3", buf.sx.inv_scale,
+                                                 buf.sw.inv_scale, buf.y), 2 * l.M * l.N * l.K)
             if mode == "dynamic":
                 timed("amax", lambda: f8lin.amax(dy, buf.sdy.amax, buf.ws, args.algo), dy.numel())
             timed("cast", lambda: f8lin.cast_transpose(dy, "e5m2", mode, buf.sdy, buf.dy8, buf.dy8t), dy.numel())
-            timed("gemm", lambda: f8lin.gemm(buf.dy8, "e5m2", buf.w8t, "e4m3", buf.sdy.inv_scale, buf.sw.inv_scale,
-                                             buf.dx), 2 * l.M * l.N * l.K)
-            timed("gemm", lambda: f8lin.gemm(buf.dy8t, "e5m2", buf.x8t, "e4m3", buf.sdy.inv_scale,
-                                             buf.sx.inv_scale, buf.dw), 2 * l.M * l.N * l.K)
+            # dgrad and wgrad in one launch, as f8lin_backward issues them
+            timed("gemm_bwd_pair", lambda: f8lin.gemm_batch(
+                [(buf.dy8, buf.w8t, buf.sdy.inv_scale, buf.sw.inv_scale, buf.dx),
+                 (buf.dy8t, buf.x8t, buf.sdy.inv_scale, buf.sx.inv_scale, buf.dw)], "e5m2", "e4m3"),
+                4 * l.M * l.N * l.K)
             if delayed:
                 f8lin.delayed_update(buf.states())
             if t == 0:
-                gemm_bytes.extend([l.M * l.K + l.N * l.K + 2 * l.M * l.N, l.M * l.N + l.N * l.K + 2 * l.M * l.K,
-                                   l.M * l.N + l.M * l.K + 2 * l.N * l.K])
+                gemm_bytes["gemm_fwd"].append(l.M * l.K + l.N * l.K + 2 * l.M * l.N)
+                gemm_bytes["gemm_bwd_pair"].append(l.M * l.N + l.N * l.K + 2 * l.M * l.K +
+                                                   l.M * l.N + l.M * l.K + 2 * l.N * l.K)
         torch.cuda.synchronize()
         if t >= args.warmup:
             for kind, a, b, units in pending:
@@ -243,11 +248,12 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                 acc[kind][1] += 1
                 acc[kind][2] += units
     k = {}
-    ms, n, el = acc["gemm"]
-    k["gemm"] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
-                 "tflops": round(el / (ms * 1e-3) / 1e12, 2),
-                 "algorithmic_bytes_per_launch": int(sum(gemm_bytes) / len(gemm_bytes)),
-                 "flops_per_launch": int(el / n)}
+    for name in ("gemm_fwd", "gemm_bwd_pair"):
+        ms, n, el = acc[name]
+        k[name] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
+                   "tflops": round(el / (ms * 1e-3) / 1e12, 2),
+                   "algorithmic_bytes_per_launch": int(sum(gemm_bytes[name]) / len(gemm_bytes[name])),
+                   "flops_per_launch": int(el / n)}
     ms, n, el = acc["cast"]
     k["cast_transpose"] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
                            "gbs": round(4 * el / (ms * 1e-3) / 1e9, 1),

@@ -188,6 +188,25 @@ int f8lin_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t
   return status_of(launch_gemm(a, fmt_a, b, fmt_b, M, N, K, inv_scale_a, inv_scale_b, c, (hipStream_t)stream));
 }
 
+int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, void *stream) {
+  static_assert(F8LIN_MAX_BATCH == kMaxGemms, "batch limit");
+  if (!d || count < 1 || count > F8LIN_MAX_BATCH) return F8LIN_EINVAL;
+  GemmDesc g[kMaxGemms];
+  Range outs[kMaxGemms], ins[4 * kMaxGemms];
+  for (int i = 0; i < count; ++i) {
+    const f8lin_gemm_desc &e = d[i];
+    F8_TRY(validate_gemm(e.a, fmt_a, e.b, fmt_b, e.M, e.N, e.K, e.inv_scale_a, e.inv_scale_b, e.c));
+    g[i] = GemmDesc{e.a, e.b, e.inv_scale_a, e.inv_scale_b, e.c, e.M, e.N, e.K};
+    outs[i] = Range{e.c, 2 * e.M * e.N};
+    ins[4 * i] = Range{e.a, e.M * e.K};
+    ins[4 * i + 1] = Range{e.b, e.N * e.K};
+    ins[4 * i + 2] = Range{e.inv_scale_a, 4};
+    ins[4 * i + 3] = Range{e.inv_scale_b, 4};
+  }
+  if (any_overlap(outs, count, ins, 4 * count)) return F8LIN_EINVAL;
+  return status_of(launch_gemms(g, count, fmt_a, fmt_b, (hipStream_t)stream));
+}
+
 int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
   if (!p) return F8LIN_EINVAL;
   const f8lin_fwd_args a = *p;

@@ -42,6 +42,14 @@ class State(ctypes.Structure):
     _fields_ = [("amax", _vp), ("scale", _vp), ("history", _vp), ("hist_meta", _vp)]
 
 
+class GemmDesc(ctypes.Structure):
+    _fields_ = [("a", _vp), ("b", _vp), ("inv_scale_a", _vp), ("inv_scale_b", _vp), ("c", _vp),
+                ("M", _i64), ("N", _i64), ("K", _i64)]
+
+
+MAX_BATCH = 2
+
+
 class FwdArgs(ctypes.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("x", _vp), ("w", _vp), ("y", _vp),
                 ("x8", _vp), ("x8t", _vp), ("w8", _vp), ("w8t", _vp), ("sx", State), ("sw", State),
@@ -62,6 +70,7 @@ _lib.f8lin_amax.argtypes = [_vp, _i64, _int, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.f8lin_cast_transpose.argtypes = [_vp, _i64, _i64, _int, _int, ctypes.POINTER(State), _vp, _vp, _vp]
 _lib.f8lin_cast_f32.argtypes = [_vp, _i64, _int, _vp, _vp]
 _lib.f8lin_gemm.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+_lib.f8lin_gemm_batch.argtypes = [ctypes.POINTER(GemmDesc), _int, _int, _int, _vp]
 _lib.f8lin_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp]
 _lib.f8lin_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp]
 _lib.f8lin_delayed_update.argtypes = [ctypes.POINTER(State), _int, _vp]
@@ -184,6 +193,20 @@ def gemm(a: torch.Tensor, fmt_a, b: torch.Tensor, fmt_b, inv_a: torch.Tensor, in
     _check(_lib.f8lin_gemm(_ptr(a, torch.uint8), _FMT[fmt_a], _ptr(b, torch.uint8), _FMT[fmt_b], M, N, K,
                            _ptr(inv_a, torch.float32), _ptr(inv_b, torch.float32), _ptr(c, torch.bfloat16),
                            _stream(stream)))
+
+
+def gemm_batch(items, fmt_a, fmt_b, stream=None):
+    """Up to MAX_BATCH GEMMs in one launch; items: (a, b, inv_a, inv_b, c) tuples
+    as for gemm(), all with the operand formats fmt_a / fmt_b."""
+    arr = (GemmDesc * max(1, len(items)))()
+    for i, (a, b, inv_a, inv_b, c) in enumerate(items):
+        M, K = a.shape
+        N = b.shape[0]
+        if b.shape[1] != K or tuple(c.shape) != (M, N):
+            raise ValueError("gemm_batch: shape mismatch")
+        arr[i] = GemmDesc(_ptr(a, torch.uint8), _ptr(b, torch.uint8), _ptr(inv_a, torch.float32),
+                          _ptr(inv_b, torch.float32), _ptr(c, torch.bfloat16), M, N, K)
+    _check(_lib.f8lin_gemm_batch(arr, len(items), _FMT[fmt_a], _FMT[fmt_b], _stream(stream)))
 
 
 def forward(x, w, y, x8, x8t, w8, w8t, sx: ScalingState, sw: ScalingState, ws, mode_x="dynamic",

@@ -136,6 +136,24 @@ int f8lin_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, void *stream)
 int f8lin_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t M, int64_t N, int64_t K,
                const float *inv_scale_a, const float *inv_scale_b, uint16_t *c, void *stream);
 
+/* Several of those GEMMs in one launch (the backward runs its dgrad and
+ * wgrad this way, pytorch/torchtitan PR #778, "Benchmarking single linear
+ * layer forward+backward performance": both backward products of the
+ * layer).  d[i] describes GEMM i exactly as the arguments of f8lin_gemm do;
+ * all of them share the operand formats fmt_a / fmt_b.  count: 1 ..
+ * F8LIN_MAX_BATCH.  Each C is computed as f8lin_gemm would (bit for bit).
+ * Errors: as f8lin_gemm for each entry; an output overlapping any other
+ * entry's input or output is F8LIN_EINVAL; nothing is launched unless every
+ * entry is valid. */
+#define F8LIN_MAX_BATCH 2
+typedef struct {
+  const uint8_t *a, *b;                      /* (M, K), (N, K) fp8 codes, K-contiguous */
+  const float *inv_scale_a, *inv_scale_b;    /* [1] each */
+  uint16_t *c;                               /* (M, N) bf16 output */
+  int64_t M, N, K;
+} f8lin_gemm_desc;
+int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, void *stream);
+
 /* Forward of the layer: X (M, K) bf16, W (N, K) bf16 -> Y (M, N) bf16.
  * Per tensor: amax (dynamic mode only), then one cast writing both layouts;
  * then Y = X8 . W8^T with the dequantisation epilogue.  x8t and w8t (and the

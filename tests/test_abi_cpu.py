@@ -34,7 +34,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_forward", "f8lin_backward",
-                     "f8lin_delayed_update", "f8lin_gemm", "f8lin_cast_f32", "f8lin_workspace_bytes",
+                     "f8lin_delayed_update", "f8lin_gemm", "f8lin_gemm_batch", "f8lin_cast_f32", "f8lin_workspace_bytes",
                      "f8lin_status_str"):
         assert required in names
 
@@ -121,6 +121,33 @@ def test_gemm_rejections(lib):
     assert f(A, 0, B + 4, 0, 32, 48, 64, AMAX, SCALE, C, None) == EALIGN
     assert f(A, 0, B, 0, 32, 48, 64, AMAX, SCALE, A, None) == EINVAL   # C aliases A
     assert f(None, 0, B, 0, 32, 48, 64, AMAX, SCALE, C, None) == EINVAL
+
+
+class GemmDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("a", "b", "inv_scale_a", "inv_scale_b", "c")] + \
+               [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+def test_gemm_batch_rejections(lib):
+    f = lib.f8lin_gemm_batch
+    f.argtypes = [ctypes.POINTER(GemmDesc), ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    C2 = C + (1 << 20)
+    ok0 = GemmDesc(A, B, AMAX, SCALE, C, 32, 48, 64)
+    ok1 = GemmDesc(B, A, AMAX, SCALE, C2, 48, 32, 64)
+    arr = (GemmDesc * 3)(ok0, ok1, ok0)
+    assert f(None, 1, 0, 0, None) == EINVAL
+    assert f(arr, 0, 0, 0, None) == EINVAL                      # empty batch
+    assert f(arr, 3, 0, 0, None) == EINVAL                      # more than F8LIN_MAX_BATCH
+    assert f(arr, 2, 0, 4, None) == EINVAL                      # bad format
+    bad = (GemmDesc * 2)(ok0, GemmDesc(B, A, AMAX, SCALE, C2, 48, 32, 65))
+    assert f(bad, 2, 0, 0, None) == ESHAPE                      # second entry's K not a multiple of 16
+    bad = (GemmDesc * 2)(ok0, GemmDesc(B, A, AMAX, SCALE, C2 + 4, 48, 32, 64))
+    assert f(bad, 2, 0, 0, None) == EALIGN
+    bad = (GemmDesc * 2)(ok0, GemmDesc(B, A, AMAX, SCALE, C + 64, 48, 32, 64))
+    assert f(bad, 2, 0, 0, None) == EINVAL                      # the two outputs overlap
+    bad = (GemmDesc * 2)(ok0, GemmDesc(B, C, AMAX, SCALE, C2, 48, 32, 64))
+    assert f(bad, 2, 0, 0, None) == EINVAL                      # second input is the first output
 
 
 class Fwd(ctypes.Structure):

@@ -245,6 +245,40 @@ def test_gemm_integer_exact_is_bit_exact(f8):
         assert torch.equal(c.cpu().view(torch.int16), want.view(torch.int16)), (M, N, K)
 
 
+@pytest.mark.parametrize("shapes", [((4096, 4096, 4096), (4096, 4096, 4096)),   # the backward pair, big tiles
+                                    ((144, 272, 400), (64, 80, 16)),            # small tiles, ragged
+                                    ((16, 4096, 4096), (4096, 4096, 16)),       # skinny dgrad + K=16 wgrad
+                                    ((0, 48, 64), (1600, 4800, 1600))])         # an empty entry
+def test_gemm_batch_equals_single_launches(f8, shapes):
+    """One launch of two GEMMs gives, bit for bit, what two f8lin_gemm calls
+    give; the second is also checked against the oracle on sampled rows."""
+    print(f"gemm_batch {shapes}", flush=True)
+    rng = np.random.default_rng(sum(sum(s) for s in shapes))
+    items, singles = [], []
+    for (M, N, K) in shapes:
+        a = torch.from_numpy(_codes(rng, (M, K), 1) & 0xF3).to(DEV)
+        b = torch.from_numpy(_codes(rng, (N, K), 0) & 0xF7).to(DEV)
+        ia = torch.tensor([0.25], dtype=torch.float32, device=DEV)
+        ib = torch.tensor([8.0], dtype=torch.float32, device=DEV)
+        c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        c1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        items.append((a, b, ia, ib, c))
+        singles.append((a, b, ia, ib, c1))
+    f8.gemm_batch(items, "e5m2", "e4m3")
+    for (a, b, ia, ib, c1) in singles:
+        f8.gemm(a, "e5m2", b, "e4m3", ia, ib, c1)
+    torch.cuda.synchronize()
+    for (_, _, _, _, c), (_, _, _, _, c1) in zip(items, singles):
+        assert torch.equal(c.view(torch.int16), c1.view(torch.int16))
+    a, b, _, _, c = items[1]
+    M = a.shape[0]
+    rows = np.unique(np.r_[0:min(M, 8), M - min(M, 8):M, rng.integers(0, M, 16)])
+    A = oracle.decode(a.cpu().numpy()[rows], 1)
+    B = oracle.decode(b.cpu().numpy(), 0)
+    ref = (A @ B.T) * 0.25 * 8.0
+    gemm_check(bf16_to_f64(c[rows]), ref, what=f"gemm_batch second entry {shapes[1]}")
+
+
 def test_gemm_k_zero_gives_zeros(f8):
     a = np.zeros((32, 0), dtype=np.uint8)
     b = np.zeros((48, 0), dtype=np.uint8)
