@@ -5,7 +5,8 @@
 // Both operands are K-contiguous ("TN"); the cast kernel writes the
 // transposed fp8 copies so that forward, dgrad and wgrad all take this form.
 // One launch runs a list of up to two such problems (the backward's dgrad
-// and wgrad go together).
+// and wgrad go together); problems with M <= 64 take a skinny kernel of
+// their own (below).
 //
 // gfx950 design (each choice measured on MI355X):
 //   * v_mfma_f32_32x32x64_f8f6f4 (the scaled builtin with zero scale operands
@@ -40,13 +41,14 @@
 //     budget: the shader clock drops from 2.4 GHz to ~1.7-2.0 GHz while this
 //     loop runs (read with s_memtime against the constant-rate counter), so
 //     bytes moved per flop cost time even when they are hidden.
-//   * Persistent workgroups walk an XCD-aware tile list.  Workgroup b runs on
+//   * Persistent workgroups walk XCD-aware tile lists.  Workgroup b runs on
 //     XCD b % 8 (round-robin dispatch), and each XCD has its own L2, so XCD x
-//     owns a contiguous range of the tile list, laid out in groups of G
-//     tile-rows walked column by column: the tiles an XCD runs at once form a
-//     compact patch whose A and B slices its L2 shares (4096^3: 96 MiB read
-//     past L2 instead of 144 MiB with row-major order).  A workgroup's output
-//     stores drain while its next tile's loads and MFMAs run.
+//     owns a contiguous eighth of each problem's tile list, laid out in groups
+//     of G tile-rows walked column by column: the tiles an XCD runs at once
+//     form a compact patch whose A and B slices its L2 shares (4096^3: 96 MiB
+//     read past L2 instead of 144 MiB with row-major order).  Giving every
+//     XCD its share of every problem keeps a batch balanced when the problems'
+//     K differ (wgrad's K is the token count).
 //   * Epilogue: acc * (inv_a * inv_b) in fp32, then two adjacent columns are
 //     brought into one lane with a DPP swap and rounded to a bf16 pair by
 //     v_cvt_pk_bf16_f32 (nearest even; checked against a software rounding on
@@ -74,11 +76,11 @@ struct Problem {
   const float *inv_a, *inv_b;
   uint16_t *c;
   int M, N, K;
-  int tiles_m, tiles_n, first;  // first: index of this problem's first tile in the list
+  int tiles_m, tiles_n;
 };
 struct Batch {
   Problem p[kMaxGemms];
-  int count, tiles;
+  int count;
 };
 
 __device__ __forceinline__ int slot128(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
@@ -116,21 +118,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   const int g = lane >> 5;  // K half within a 64-byte sub-step
   const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
 
-  // This workgroup's share of the tile list: XCD x owns [start, start + len)
-  // and its wx workgroups take every wx-th tile of it.
+  // This workgroup's share of the tiles: XCD x owns a contiguous 1/8 of each
+  // problem's tile list (so problems of different K stay balanced across
+  // XCDs), and its wx workgroups take every wx-th tile of that share.
   const int xcd = (int)blockIdx.x % kXcds, local_wg = (int)blockIdx.x / kXcds;
   const int nwg = (int)gridDim.x;
-  const int per = batch.tiles / kXcds, rem = batch.tiles % kXcds;
-  const int start = xcd * per + min(xcd, rem), len = per + (xcd < rem ? 1 : 0);
   const int wx = nwg / kXcds + (xcd < nwg % kXcds ? 1 : 0);
+  int start[kMaxGemms], len[kMaxGemms], total = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxGemms; ++i) {
+    const int T = i < batch.count ? batch.p[i].tiles_m * batch.p[i].tiles_n : 0;
+    const int per = T / kXcds, rem = T % kXcds;
+    start[i] = xcd * per + min(xcd, rem);
+    len[i] = per + (xcd < rem ? 1 : 0);
+    total += len[i];
+  }
 
-  for (int it = local_wg; it < len; it += wx) {
-    const int t = start + it;
-    const int pi = (batch.count > 1 && t >= batch.p[1].first) ? 1 : 0;
+  for (int it = local_wg; it < total; it += wx) {
+    const int pi = it < len[0] ? 0 : 1;
+    const int t = start[pi] + (pi ? it - len[0] : it);
     const Problem P = batch.p[pi];
     const int M = P.M, N = P.N, K = P.K;
     int tm, tn;
-    tile_coords<G>(t - P.first, P.tiles_m, P.tiles_n, tm, tn);
+    tile_coords<G>(t, P.tiles_m, P.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
     const __amdgpu_buffer_rsrc_t rsa =
@@ -315,8 +325,100 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   }
 }
 
+// Skinny problems (M <= 64: the forward and dgrad of a handful of tokens)
+// are bound by reading B once (N x K bytes) at HBM speed; the tiled kernel
+// above would give them only N / 128 workgroups.  Here one workgroup of four
+// waves owns 16 rows of B (16 output columns), so N / 16 workgroups stream
+// B; the waves split K in 128-byte blocks (wave w takes blocks w, w + 4, ...),
+// load both operands straight into registers, U blocks in flight per wave,
+// and run v_mfma_f32_16x16x128_f8f6f4 once per 16-row block of A (lane l
+// feeds row l % 16 and K bytes 32 * (l / 16) .. +32 of both operands; the
+// accumulator of lane l holds rows 4 * (l / 16) + i, column l % 16).  The
+// four waves' partial sums meet in LDS.
+template <int FA, int FB, int MT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const Problem P) {
+  constexpr int U = MT <= 2 ? 8 : 4;
+  typedef float v4f_t __attribute__((ext_vector_type(4)));
+  __shared__ v4f_t red[4][MT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = (int)blockIdx.x * 16;
+  const int M = P.M, N = P.N, K = P.K;
+  const int rows_b = min(16, N - n0);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)P.a, (short)0, M * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(P.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+  const int r = lane & 15, kq = (lane >> 4) * 32;
+  const int nkb = (K + kBK - 1) / kBK;
+  v4f_t acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto load = [&](__amdgpu_buffer_rsrc_t rs, int row, int kb, int k) {
+    // 32 bytes of `row` at K offset k of block kb; chunks past K (or blocks
+    // past the end) point outside the range and read as zeros
+    const int k0 = kb * kBK + k;
+    const int o0 = (kb < nkb && k0 < K) ? row * K + k0 : kOutOfRange;
+    const int o1 = (kb < nkb && k0 + 16 < K) ? row * K + k0 + 16 : kOutOfRange;
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o0, 0, 0));
+    const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o1, 0, 0));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  for (int kb0 = wave; kb0 < nkb; kb0 += 4 * U) {
+    v8i fb[U], fa[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      fb[u] = load(rsb, r, kb0 + 4 * u, kq);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) fa[u][m] = load(rsa, m * 16 + r, kb0 + 4 * u, kq);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all U blocks in flight before the first MFMA
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[u][m], fb[u], acc[m], FA, FB, 0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+  __syncthreads();
+  if (wave == 0) {
+    const float alpha = P.inv_a[0] * P.inv_b[0];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const v4f_t t = red[0][m][lane] + red[1][m][lane] + red[2][m][lane] + red[3][m][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + 4 * (lane >> 4) + i, col = n0 + (lane & 15);
+        if (row < M && col < N) P.c[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(t[i] * alpha);
+      }
+    }
+  }
+}
+
+constexpr int kSkinnyMaxM = 64;
+
+template <int FA, int FB>
+void launch_skinny(const Problem &p, hipStream_t stream) {
+  const unsigned grid = (unsigned)((p.N + 15) / 16);
+  switch ((p.M + 15) / 16) {
+    case 1: gemm_skinny_kernel<FA, FB, 1><<<grid, 256, 0, stream>>>(p); break;
+    case 2: gemm_skinny_kernel<FA, FB, 2><<<grid, 256, 0, stream>>>(p); break;
+    case 3: gemm_skinny_kernel<FA, FB, 3><<<grid, 256, 0, stream>>>(p); break;
+    default: gemm_skinny_kernel<FA, FB, 4><<<grid, 256, 0, stream>>>(p); break;
+  }
+}
+
 template <int FA, int FB>
 void launch_fmt(Batch &b, hipStream_t stream) {
+  // skinny problems get their own launches; the rest share one
+  Batch rest{};
+  for (int i = 0; i < b.count; ++i) {
+    if (b.p[i].M <= kSkinnyMaxM)
+      launch_skinny<FA, FB>(b.p[i], stream);
+    else
+      rest.p[rest.count++] = b.p[i];
+  }
+  b = rest;
+  if (b.count == 0) return;
   int64_t big = 0;
   for (int i = 0; i < b.count; ++i) big += (int64_t)((b.p[i].M + 255) / 256) * ((b.p[i].N + 255) / 256);
   const bool use_big = big >= kCUs;
@@ -326,10 +428,8 @@ void launch_fmt(Batch &b, hipStream_t stream) {
     Problem &p = b.p[i];
     p.tiles_m = (p.M + bm - 1) / bm;
     p.tiles_n = (p.N + bm - 1) / bm;
-    p.first = tiles;
     tiles += p.tiles_m * p.tiles_n;
   }
-  b.tiles = tiles;
   if (tiles == 0) return;
   if (use_big) {
     gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(b);
