@@ -166,11 +166,15 @@ def encode_bits_range(lo: int, count: int, fmt: int) -> np.ndarray:
 # decodes exactly to fp64, each product of two fp8 values is exact in fp64,
 # the sums are fp64, and the result is divided by both tensor scales.
 
-def forward_ref(x8, w8, sx, sw):
-    """Y (M, N) = (X8 . W8^T) / (s_x s_w), X8 (M, K) e4m3, W8 (N, K) e4m3."""
+def forward_ref(x8, w8, sx, sw, bias_bits=None):
+    """Y (M, N) = (X8 . W8^T) / (s_x s_w) [+ b], X8 (M, K) e4m3, W8 (N, K) e4m3,
+    b (N,) bf16 bits added to every row."""
     a = decode(x8, E4M3)
     b = decode(w8, E4M3)
-    return (a @ b.T) / np.float64(sx) / np.float64(sw)
+    y = (a @ b.T) / np.float64(sx) / np.float64(sw)
+    if bias_bits is not None:
+        y = y + bf16_to_f64(bias_bits)[None, :]
+    return y
 
 
 def dgrad_ref(dy8, w8, sdy, sw):
@@ -219,6 +223,30 @@ def wgrad_ref_at(dy8, x8, sdy, sx, rows, cols):
     return _dot_rows(a, b) / np.float64(sdy) / np.float64(sx)
 
 
+# -------------------------------------------------------------------- bias
+# The linear layers of the GPT-1.5B repro carry a bias (pytorch/ao issue
+# #1297, repro script: the nn.Linear layers of CausalSelfAttention and
+# GPTBlock keep nn.Linear's default bias).  Such a layer computes
+# Y = X W^T + b, and its backward produces the bias gradient: the sum of dY
+# over the token rows.  Both are written out from that definition; the bias
+# and its gradient stay in bf16 (reading: the pages cast only the three GEMM
+# operands to fp8).
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of bf16 bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dbias_ref(dy_bits: np.ndarray) -> np.ndarray:
+    """db[n] = sum over rows m of dY[m, n], in fp64 (dY (M, N) bf16 bits)."""
+    d = bf16_to_f64(dy_bits)
+    out = np.zeros(d.shape[1], dtype=np.float64)
+    for m in range(d.shape[0]):  # rows in order: a plain running sum per column
+        out += d[m]
+    return out
+
+
 # --------------------------------------------------------- delayed scaling
 
 class DelayedHistory:
@@ -262,20 +290,24 @@ def _quantize(t_bits, fmt, amax_for_scale=None):
     return {"amax": a_now, "scale": s, "inv_scale": inv, "q": q, "qt": qt, "saturated": nsat}
 
 
-def linear_step(x_bits, w_bits, dy_bits, *, amax_x=None, amax_w=None, amax_dy=None, gemms=True):
+def linear_step(x_bits, w_bits, dy_bits, *, amax_x=None, amax_w=None, amax_dy=None, gemms=True,
+                bias_bits=None):
     """One forward + backward of a tensorwise-scaled Float8Linear.
 
     amax_* override the amax a tensor's scale is computed from (delayed
     scaling passes the history's amax); None means dynamic scaling.  Returns
-    the per-tensor results and, if `gemms`, the fp64 Y, dX and dW."""
+    the per-tensor results and, if `gemms`, the fp64 Y, dX and dW.  With a
+    bias (bf16 bits, (N,)), Y includes it and "dbias" holds its gradient."""
     qx = _quantize(x_bits, E4M3, amax_x)
     qw = _quantize(w_bits, E4M3, amax_w)
     qdy = _quantize(dy_bits, E5M2, amax_dy)
     out = {"x": qx, "w": qw, "dy": qdy}
     if gemms:
-        out["y"] = forward_ref(qx["q"], qw["q"], qx["scale"], qw["scale"])
+        out["y"] = forward_ref(qx["q"], qw["q"], qx["scale"], qw["scale"], bias_bits)
         out["dx"] = dgrad_ref(qdy["q"], qw["q"], qdy["scale"], qw["scale"])
         out["dw"] = wgrad_ref(qdy["q"], qx["q"], qdy["scale"], qx["scale"])
+    if bias_bits is not None:
+        out["dbias"] = dbias_ref(dy_bits)
     return out
 
 

@@ -406,6 +406,48 @@ def test_gemm_refs_against_exact_rational_arithmetic():
                 assert abs(Fraction(float(got[i, j])) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
 
 
+def test_bias_refs_against_exact_rational_arithmetic():
+    """Y = X8 W8^T / (s_x s_w) + b and db = column sums of dY, against
+    Fractions written from the definitions."""
+    rng = np.random.default_rng(23)
+    M, N, K = 6, 5, 7
+    x8 = _codes(rng, (M, K), E4M3)
+    w8 = _codes(rng, (N, K), E4M3)
+    sx, sw = np.float32(2.5), np.float32(0.75)
+    bias = rng.integers(0, 0x10000, N).astype(np.uint16)
+    bias[(bias & 0x7F80) == 0x7F80] = 0x3F80  # finite biases only
+    dy = rng.integers(0, 0x10000, (M, N)).astype(np.uint16)
+    dy[(dy & 0x7F80) == 0x7F80] = 0xBF00
+    bvals = [Fraction(float(v)) for v in _bf16_to_f32(bias)]
+    y = _exact_matmul(_frac(x8, E4M3), _frac(w8, E4M3), transpose_b=True)
+    den = Fraction(float(sx)) * Fraction(float(sw))
+    got = oracle.forward_ref(x8, w8, sx, sw, bias)
+    for i in range(M):
+        for j in range(N):
+            want = y[i][j] / den + bvals[j]
+            assert abs(Fraction(float(got[i, j])) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+    dvals = [[Fraction(float(v)) for v in _bf16_to_f32(row)] for row in dy]
+    db = oracle.dbias_ref(dy)
+    for j in range(N):
+        want = sum((dvals[i][j] for i in range(M)), Fraction(0))
+        assert abs(Fraction(float(db[j])) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+
+
+def test_dbias_ref_invariants():
+    # ones -> the row count; row order does not matter; a transposed input
+    # would give the row sums instead (a distinct shape catches the swap)
+    M, N = 37, 11
+    ones = np.full((M, N), 0x3F80, dtype=np.uint16)
+    assert np.array_equal(oracle.dbias_ref(ones), np.full(N, float(M)))
+    rng = np.random.default_rng(5)
+    dy = (rng.standard_normal((M, N)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    perm = rng.permutation(M)
+    assert np.allclose(oracle.dbias_ref(dy), oracle.dbias_ref(dy[perm]), rtol=0, atol=1e-12)
+    assert oracle.dbias_ref(dy).shape == (N,)
+    ref_sum = _bf16_to_f32(dy.reshape(-1)).reshape(M, N).astype(np.float64).sum(axis=0)
+    assert np.allclose(oracle.dbias_ref(dy), ref_sum, rtol=1e-15, atol=1e-12)
+
+
 def test_gemm_sampled_entries_equal_full_refs():
     rng = np.random.default_rng(22)
     M, N, K = 33, 47, 65
