@@ -128,6 +128,10 @@ int validate_gemm(const uint8_t *a, int fa, const uint8_t *b, int fb, int64_t M,
   return F8LIN_OK;
 }
 
+// Row tiles of the cast kernel: the number of per-tile column sums the bias
+// gradient reduces (one when dY has no rows: that tile's sums are zeros).
+int64_t dbias_tiles(int64_t M) { return M > 0 ? (M + kCastTile - 1) / kCastTile : 1; }
+
 }  // namespace
 }  // namespace f8lin
 
@@ -136,6 +140,11 @@ using namespace f8lin;
 extern "C" {
 
 size_t f8lin_workspace_bytes(void) { return kWorkspaceBytes; }
+
+size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N) {
+  if (M < 0 || N < 0) return 0;
+  return (size_t)dbias_tiles(M) * (size_t)N * sizeof(float);
+}
 
 const char *f8lin_status_str(int status) {
   switch (status) {
@@ -222,7 +231,7 @@ int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
       missing(a.w, a.N * a.K) || missing(a.w8, a.N * a.K) || missing(a.w8t, a.N * a.K) || missing(a.y, a.M * a.N))
     return F8LIN_EINVAL;
   if (!aligned16(a.x) || !aligned16(a.w) || !aligned16(a.y) || !aligned16(a.x8) || !aligned16(a.x8t) ||
-      !aligned16(a.w8) || !aligned16(a.w8t))
+      !aligned16(a.w8) || !aligned16(a.w8t) || !aligned16(a.bias))
     return F8LIN_EALIGN;
   const bool need_ws = a.mode_x == F8LIN_DYNAMIC || a.mode_w == F8LIN_DYNAMIC;
   if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
@@ -231,9 +240,12 @@ int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
                           {a.w8, nk},      {a.w8t, nk},  {a.sx.scale, 8},
                           {a.sw.scale, 8}, {a.sx.amax, 4}, {a.sw.amax, 4},
                           {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0}};
-  const Range ins[4] = {{a.x, 2 * mk}, {a.w, 2 * nk}, {a.sx.history, a.mode_x == F8LIN_DELAYED ? 64 : 0},
-                        {a.sw.history, a.mode_w == F8LIN_DELAYED ? 64 : 0}};
-  if (any_overlap(outs, 10, ins, 4)) return F8LIN_EINVAL;
+  const Range ins[5] = {{a.x, 2 * mk},
+                        {a.w, 2 * nk},
+                        {a.sx.history, a.mode_x == F8LIN_DELAYED ? 64 : 0},
+                        {a.sw.history, a.mode_w == F8LIN_DELAYED ? 64 : 0},
+                        {a.bias, a.bias ? 2 * a.N : 0}};
+  if (any_overlap(outs, 10, ins, 5)) return F8LIN_EINVAL;
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
@@ -266,8 +278,8 @@ int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
     F8_TRY(status_of(launch_cast(&cx, 1, F8LIN_E4M3, a.mode_x, s)));
     F8_TRY(status_of(launch_cast(&cw, 1, F8LIN_E4M3, a.mode_w, s)));
   }
-  return status_of(
-      launch_gemm(a.x8, F8LIN_E4M3, a.w8, F8LIN_E4M3, a.M, a.N, a.K, a.sx.scale + 1, a.sw.scale + 1, a.y, s));
+  const GemmDesc g = {a.x8, a.w8, a.sx.scale + 1, a.sw.scale + 1, a.y, a.M, a.N, a.K, a.bias};
+  return status_of(launch_gemms(&g, 1, F8LIN_E4M3, F8LIN_E4M3, s));
 }
 
 int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
@@ -285,20 +297,30 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
       missing(a.dw, a.N * a.K))
     return F8LIN_EINVAL;
   if (!aligned16(a.dy) || !aligned16(a.x8t) || !aligned16(a.w8t) || !aligned16(a.dx) || !aligned16(a.dw) ||
-      !aligned16(a.dy8) || !aligned16(a.dy8t))
+      !aligned16(a.dy8) || !aligned16(a.dy8t) || !aligned16(a.dbias) || !aligned16(a.dbias_ws))
     return F8LIN_EALIGN;
   const bool need_ws = a.mode_dy == F8LIN_DYNAMIC;
   if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
+  const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
+  if (db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
   const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
-  const Range outs[7] = {{a.dx, 2 * mk},     {a.dw, 2 * nk},   {a.dy8, mn}, {a.dy8t, mn},
-                         {a.sdy.scale, 8}, {a.sdy.amax, 4}, {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0}};
+  const Range outs[9] = {{a.dx, 2 * mk},
+                         {a.dw, 2 * nk},
+                         {a.dy8, mn},
+                         {a.dy8t, mn},
+                         {a.sdy.scale, 8},
+                         {a.sdy.amax, 4},
+                         {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0},
+                         {a.dbias, a.dbias ? 2 * a.N : 0},
+                         {a.dbias_ws, db_ws}};
   const Range ins[6] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
                         {a.sx.scale, 8}, {a.sw.scale, 8}, {a.sdy.history, a.mode_dy == F8LIN_DELAYED ? 64 : 0}};
-  if (any_overlap(outs, 7, ins, 6)) return F8LIN_EINVAL;
+  if (any_overlap(outs, 9, ins, 6)) return F8LIN_EINVAL;
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
   CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
+  if (a.dbias) cdy.colsum = a.dbias_ws;  // the cast also sums dY's columns per 128-row tile
   if (a.mode_dy == F8LIN_DYNAMIC) {
     const AmaxTensor t = {a.dy, mn, a.sdy.amax};
     if (a.algo == F8LIN_AMAX_TWOPASS)
@@ -307,6 +329,7 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
       F8_TRY(status_of(launch_amax(&t, 1, a.algo, ws, s)));
   }
   F8_TRY(status_of(launch_cast(&cdy, 1, F8LIN_E5M2, a.mode_dy, s)));
+  if (a.dbias) F8_TRY(status_of(launch_dbias(a.dbias_ws, dbias_tiles(a.M), a.N, a.dbias, s)));
   // One launch for both GEMMs:
   //   dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N;
   //   dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.

@@ -34,7 +34,7 @@
 namespace f8lin {
 namespace {
 
-constexpr int kTile = 128;
+constexpr int kTile = kCastTile;
 constexpr int kThreads = 256;
 static_assert(kThreads / 64 == 4 && kMaxGrid <= kThreads, "partials reduction layout");
 
@@ -71,6 +71,7 @@ struct CastJob {
   float *amax_acc;        // delayed: where this step's amax accumulates
   float *scale_out;       // {scale, 1/scale}
   uint8_t *q, *qt;
+  float *colsum;          // per-tile column sums (bias gradient), or null
   int tiles_x;
   int first;
 };
@@ -83,6 +84,7 @@ template <int FMT, int MODE, bool WRITE_T>
 __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs jobs) {
   __shared__ uint32_t tile[kTile * kTile / 4];
   __shared__ uint32_t red[kThreads / 64];
+  __shared__ float colred[kThreads / 64][kTile];
   constexpr float fm = fmt_max<FMT>();
   const int job = (jobs.count > 1 && (int)blockIdx.x >= jobs.j[1].first) ? 1 : 0;
   const CastJob &jb = jobs.j[job];
@@ -112,6 +114,25 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
       in[p][0] = u32x4{0, 0, 0, 0};
       in[p][1] = u32x4{0, 0, 0, 0};
     }
+  }
+
+  // Column sums of this thread's four rows (bias gradient), in row order.
+  float cs[16];
+  const bool want_cs = jb.colsum != nullptr;
+  if (want_cs) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cs[e] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w4[4] = {in[p][h].x, in[p][h].y, in[p][h].z, in[p][h].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          cs[8 * h + 2 * w] += bf16_lo(w4[w]);
+          cs[8 * h + 2 * w + 1] += bf16_hi(w4[w]);
+        }
+      }
   }
 
   // The scale (after the tile's loads are in flight).
@@ -209,6 +230,26 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
       for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4 *>(qt + (qrow + b) * rows + qcol) = out[b];
     }
   }
+  // Bias gradient: this tile's column sums.  The 32 threads of one column
+  // group are lanes c16 + 8 * (0..7) of the four waves: a fixed xor tree
+  // inside each wave, then the four waves in order -- the same order on every
+  // run.
+  if (want_cs) {
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cs[e] += __shfl_xor(cs[e], off, 64);
+    const int lane = t & 63, wave = t >> 6;
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) colred[wave][lane * 16 + e] = cs[e];
+    }
+    __syncthreads();
+    if (t < kTile && col0 + t < cols) {
+      const float v = ((colred[0][t] + colred[1][t]) + colred[2][t]) + colred[3][t];
+      jb.colsum[(row0 / kTile) * cols + col0 + t] = v;
+    }
+  }
 }
 
 template <int FMT>
@@ -222,6 +263,38 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const float *__restr
         cvt4<FMT>(saturate(f.x, fm), saturate(f.y, fm), saturate(f.z, fm), saturate(f.w, fm));
   } else {
     for (int64_t j = i; j < n; ++j) q[j] = (uint8_t)(cvt4<FMT>(saturate(v[j], fm), 0.f, 0.f, 0.f) & 0xFFu);
+  }
+}
+
+// Bias gradient from the per-tile column sums: workgroup of 256 threads per
+// 32 columns; thread (column c, group g) sums tiles g, g + 8, ... in order,
+// then thread (c, 0) adds the eight group sums in order: a fixed order on
+// every run.
+constexpr int kDbCols = 32, kDbGroups = 8;
+__global__ __launch_bounds__(kDbCols * kDbGroups) void dbias_kernel(const float *__restrict__ colsum, int64_t tiles,
+                                                                     int64_t n, uint16_t *__restrict__ db) {
+  __shared__ float part[kDbGroups][kDbCols];
+  const int c = threadIdx.x % kDbCols, g = threadIdx.x / kDbCols;
+  const int64_t col = (int64_t)blockIdx.x * kDbCols + c;
+  float s = 0.0f;
+  if (col < n) {
+    int64_t t = g;
+    for (; t + 7 * kDbGroups < tiles; t += 8 * kDbGroups) {  // eight loads in flight, added in order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = colsum[(t + u * kDbGroups) * n + col];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; t < tiles; t += kDbGroups) s += colsum[t * n + col];
+  }
+  part[g][c] = s;
+  __syncthreads();
+  if (g == 0 && col < n) {
+    float r = part[0][c];
+#pragma unroll
+    for (int i = 1; i < kDbGroups; ++i) r += part[i][c];
+    db[col] = (uint16_t)f32_to_bf16_rne(r);
   }
 }
 
@@ -248,8 +321,8 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
     const int64_t gx = t.cols > 0 ? (t.cols + kTile - 1) / kTile : 1;
     const int64_t gy = t.rows > 0 ? (t.rows + kTile - 1) / kTile : 1;
     jobs.j[i] = CastJob{t.x,          t.rows,       t.cols,      t.st->amax, t.partials, t.npartials,
-                        t.st->history, t.st->amax, t.st->scale, t.q,        t.qt,       (int)gx,
-                        (int)total};
+                        t.st->history, t.st->amax, t.st->scale, t.q,        t.qt,       t.colsum,
+                        (int)gx,       (int)total};
     total += gx * gy;
   }
   // (An empty tensor may pass a null qt; its workgroup writes no rows.)
@@ -263,6 +336,13 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
     if (mode == F8LIN_DYNAMIC) launch_ct<1, F8LIN_DYNAMIC>(grid, jobs, write_t, stream);
     else launch_ct<1, F8LIN_DELAYED>(grid, jobs, write_t, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dbias(const float *colsum, int64_t tiles, int64_t n_cols, uint16_t *db, hipStream_t stream) {
+  if (n_cols == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n_cols + kDbCols - 1) / kDbCols);
+  dbias_kernel<<<grid, kDbCols * kDbGroups, 0, stream>>>(colsum, tiles, n_cols, db);
   return hipGetLastError();
 }
 

@@ -49,7 +49,9 @@
 //     read past L2 instead of 144 MiB with row-major order).  Giving every
 //     XCD its share of every problem keeps a batch balanced when the problems'
 //     K differ (wgrad's K is the token count).
-//   * Epilogue: acc * (inv_a * inv_b) in fp32, then two adjacent columns are
+//   * Epilogue: acc * (inv_a * inv_b) in fp32 (+ the bias in fp32, when the
+//     layer has one: pytorch/ao issue #1297, repro script, whose nn.Linear
+//     layers keep their default bias), then two adjacent columns are
 //     brought into one lane with a DPP swap and rounded to a bf16 pair by
 //     v_cvt_pk_bf16_f32 (nearest even; checked against a software rounding on
 //     all 2^32 binary32 patterns), staged through LDS per wave and written as
@@ -75,6 +77,7 @@ struct Problem {
   const uint8_t *a, *b;
   const float *inv_a, *inv_b;
   uint16_t *c;
+  const uint16_t *bias;  // (N) bf16 or null
   int M, N, K;
   int tiles_m, tiles_n;
 };
@@ -293,6 +296,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     const float alpha = P.inv_a[0] * P.inv_b[0];
     uint8_t *wreg = smem + wave * (WTM * RB);
     const bool odd = lane & 1;
+    // bias of this lane's column pair (cpair, cpair + 1) of each 32-column tile j
+    float bias_lo[TN], bias_hi[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int gc = n0 + wn + j * 32 + (lane & 30);
+      uint32_t bw = 0;
+      if (P.bias && gc < N) bw = *(const uint32_t *)(P.bias + gc);
+      bias_lo[j] = __uint_as_float(bw << 16);
+      bias_hi[j] = __uint_as_float(bw & 0xFFFF0000u);
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -303,7 +316,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
           const float ve = acc[i][j][2 * k] * alpha, vo = acc[i][j][2 * k + 1] * alpha;
           const float send = odd ? ve : vo;
           const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
-          const f32x2 pair = odd ? f32x2{recv, vo} : f32x2{ve, recv};
+          const f32x2 pair = odd ? f32x2{recv + bias_lo[j], vo + bias_hi[j]} : f32x2{ve + bias_lo[j], recv + bias_hi[j]};
           const int v = 2 * k + (odd ? 1 : 0);
           const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           *(bf16x2 *)(wreg + row * RB + ((cpair * 2) ^ (((row >> 2) & 1) << 6))) =
@@ -388,7 +401,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const Problem P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + 4 * (lane >> 4) + i, col = n0 + (lane & 15);
-        if (row < M && col < N) P.c[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(t[i] * alpha);
+        const float bv = P.bias ? __uint_as_float((uint32_t)P.bias[col < N ? col : 0] << 16) : 0.0f;
+        if (row < M && col < N) P.c[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(t[i] * alpha + bv);
       }
     }
   }
@@ -450,6 +464,7 @@ hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipS
     p.inv_a = d[i].inv_a;
     p.inv_b = d[i].inv_b;
     p.c = d[i].c;
+    p.bias = d[i].bias;
     p.M = (int)d[i].M;
     p.N = (int)d[i].N;
     p.K = (int)d[i].K;
@@ -468,7 +483,7 @@ hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipS
 
 hipError_t launch_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t M, int64_t N,
                        int64_t K, const float *inv_a, const float *inv_b, uint16_t *c, hipStream_t stream) {
-  const GemmDesc d{a, b, inv_a, inv_b, c, M, N, K};
+  const GemmDesc d{a, b, inv_a, inv_b, c, M, N, K, nullptr};
   return launch_gemms(&d, 1, fmt_a, fmt_b, stream);
 }
 

@@ -40,8 +40,16 @@ struct CastTensor {
   // st->amax is written), or null to read st->amax
   const uint32_t *partials = nullptr;
   int npartials = 0;
+  // if set (e5m2 only): fp32 column sums of x over each 128-row tile,
+  // colsum[tile_row * cols + col], for the bias gradient
+  float *colsum = nullptr;
 };
 hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream);
+
+// Bias gradient: db[n] = bf16(sum over t < tiles of colsum[t * n_cols + n]),
+// summed in order of t.
+hipError_t launch_dbias(const float *colsum, int64_t tiles, int64_t n_cols, uint16_t *db, hipStream_t stream);
+constexpr int kCastTile = 128;
 
 hipError_t launch_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, hipStream_t stream);
 
@@ -56,6 +64,7 @@ struct GemmDesc {
   const float *inv_a, *inv_b;
   uint16_t *c;
   int64_t M, N, K;
+  const uint16_t *bias = nullptr;  // (N) bf16 added to every row, or null
 };
 hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream);
 

@@ -53,17 +53,21 @@ MAX_BATCH = 2
 class FwdArgs(ctypes.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("x", _vp), ("w", _vp), ("y", _vp),
                 ("x8", _vp), ("x8t", _vp), ("w8", _vp), ("w8t", _vp), ("sx", State), ("sw", State),
-                ("mode_x", _int), ("mode_w", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
+                ("mode_x", _int), ("mode_w", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
+                ("bias", _vp)]
 
 
 class BwdArgs(ctypes.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("dy", _vp), ("x8t", _vp), ("w8t", _vp),
                 ("dx", _vp), ("dw", _vp), ("dy8", _vp), ("dy8t", _vp), ("sx", State), ("sw", State),
-                ("sdy", State), ("mode_dy", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t)]
+                ("sdy", State), ("mode_dy", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
+                ("dbias", _vp), ("dbias_ws", _vp), ("dbias_ws_bytes", ctypes.c_size_t)]
 
 
 _lib.f8lin_workspace_bytes.argtypes = []
 _lib.f8lin_workspace_bytes.restype = ctypes.c_size_t
+_lib.f8lin_dbias_workspace_bytes.argtypes = [_i64, _i64]
+_lib.f8lin_dbias_workspace_bytes.restype = ctypes.c_size_t
 _lib.f8lin_status_str.argtypes = [_int]
 _lib.f8lin_status_str.restype = ctypes.c_char_p
 _lib.f8lin_amax.argtypes = [_vp, _i64, _int, _vp, _vp, ctypes.c_size_t, _vp]
@@ -110,6 +114,15 @@ def _ptr(t: Optional[torch.Tensor], dtype=None) -> Optional[int]:
 
 def workspace_bytes() -> int:
     return int(_lib.f8lin_workspace_bytes())
+
+
+def dbias_workspace_bytes(M: int, N: int) -> int:
+    return int(_lib.f8lin_dbias_workspace_bytes(M, N))
+
+
+def new_dbias_workspace(M: int, N: int, device="cuda") -> torch.Tensor:
+    """Scratch (float32, no initialisation needed) for the bias gradient of an (M, N) dY."""
+    return torch.empty(max(1, dbias_workspace_bytes(M, N) // 4), dtype=torch.float32, device=device)
 
 
 def status_str(status: int) -> str:
@@ -210,28 +223,34 @@ def gemm_batch(items, fmt_a, fmt_b, stream=None):
 
 
 def forward(x, w, y, x8, x8t, w8, w8t, sx: ScalingState, sw: ScalingState, ws, mode_x="dynamic",
-            mode_w="dynamic", algo="atomic", stream=None):
+            mode_w="dynamic", algo="atomic", stream=None, bias=None):
     M, K = x.shape
     N = w.shape[0]
+    if bias is not None and tuple(bias.shape) != (N,):
+        raise ValueError("forward: bias must have shape (N,)")
     a = FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
                 _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
                 sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
-                ws.numel() * ws.element_size())
+                ws.numel() * ws.element_size(), None if bias is None else _ptr(bias, torch.bfloat16))
     if w.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError("forward: shape mismatch")
     _check(_lib.f8lin_forward(ctypes.byref(a), _stream(stream)))
 
 
 def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState, sdy: ScalingState, ws,
-             mode_dy="dynamic", algo="atomic", stream=None):
+             mode_dy="dynamic", algo="atomic", stream=None, dbias=None, dbias_ws=None):
     M, N = dy.shape
     K = x8t.shape[0]
     if tuple(dx.shape) != (M, K) or tuple(dw.shape) != (N, K) or tuple(w8t.shape) != (K, N):
         raise ValueError("backward: shape mismatch")
+    if dbias is not None and tuple(dbias.shape) != (N,):
+        raise ValueError("backward: dbias must have shape (N,)")
     a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr(x8t, torch.uint8), _ptr(w8t, torch.uint8),
                 _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr(dy8t, torch.uint8),
                 sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], _ptr(ws),
-                ws.numel() * ws.element_size())
+                ws.numel() * ws.element_size(), None if dbias is None else _ptr(dbias, torch.bfloat16),
+                None if dbias_ws is None else _ptr(dbias_ws, torch.float32),
+                0 if dbias_ws is None else dbias_ws.numel() * 4)
     _check(_lib.f8lin_backward(ctypes.byref(a), _stream(stream)))
 
 
@@ -246,7 +265,7 @@ class LinearBuffers:
     """Every device buffer one Float8Linear forward + backward needs, for
     X (M, K), W (N, K), dY (M, N); allocated once with torch (plumbing)."""
 
-    def __init__(self, M: int, N: int, K: int, device="cuda"):
+    def __init__(self, M: int, N: int, K: int, device="cuda", with_bias: bool = False):
         u8 = dict(dtype=torch.uint8, device=device)
         bf = dict(dtype=torch.bfloat16, device=device)
         self.M, self.N, self.K = M, N, K
@@ -263,15 +282,17 @@ class LinearBuffers:
         self.sw = ScalingState(device)
         self.sdy = ScalingState(device)
         self.ws = new_workspace(device)
+        self.dbias = torch.empty((N,), **bf) if with_bias else None
+        self.dbias_ws = new_dbias_workspace(M, N, device) if with_bias else None
 
-    def forward(self, x, w, mode="dynamic", algo="atomic", stream=None):
+    def forward(self, x, w, mode="dynamic", algo="atomic", stream=None, bias=None):
         forward(x, w, self.y, self.x8, self.x8t, self.w8, self.w8t, self.sx, self.sw, self.ws, mode, mode, algo,
-                stream)
+                stream, bias)
         return self.y
 
     def backward(self, dy, mode="dynamic", algo="atomic", stream=None):
         backward(dy, self.x8t, self.w8t, self.dx, self.dw, self.dy8, self.dy8t, self.sx, self.sw, self.sdy,
-                 self.ws, mode, algo, stream)
+                 self.ws, mode, algo, stream, self.dbias, self.dbias_ws)
         return self.dx, self.dw
 
     def states(self):

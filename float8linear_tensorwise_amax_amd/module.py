@@ -11,8 +11,10 @@ this file only allocates tensors and marshals arguments.
 
 Shapes: in_features and out_features must be multiples of 16.  The token
 dimension may be anything: it is zero-padded to a multiple of 16, which is
-exact (zero rows raise no amax, add nothing to dW, and their Y / dX rows are
-dropped).  Bias is not supported by the kernels yet.
+exact (zero rows raise no amax, add nothing to dW or to the bias gradient,
+and their Y / dX rows are dropped).  A bias (the repro's nn.Linear layers
+keep theirs) is added in the GEMM epilogue and its gradient is summed in the
+backward's cast pass.
 """
 from dataclasses import dataclass, field
 from typing import Dict, Optional
@@ -50,10 +52,11 @@ def _pad_rows(t: torch.Tensor) -> torch.Tensor:
 
 class _Float8LinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x2d, weight, layer):
+    def forward(ctx, x2d, weight, bias, layer):
         M0 = x2d.shape[0]
         x = _pad_rows(x2d.to(torch.bfloat16))
         w = weight.to(torch.bfloat16).contiguous()
+        b = None if bias is None else bias.to(torch.bfloat16).contiguous()
         M, K = x.shape
         N = w.shape[0]
         dev = x.device
@@ -66,13 +69,14 @@ class _Float8LinearFn(torch.autograd.Function):
         mode_x = layer._mode("x")
         mode_w = layer._mode("w")
         f8lin.forward(x, w, y, x8, x8t, w8, w8t, layer.sx, layer.sw, layer.ws, mode_x, mode_w,
-                      layer.config.amax_algo)
+                      layer.config.amax_algo, bias=b)
         # backward must use the scales these fp8 copies were made with, even if
         # the layer runs forward again before it (micro-batches, recomputation)
         ctx.save_for_backward(x8t, w8t, layer.sx.scale.clone(), layer.sw.scale.clone())
         ctx.layer = layer
         ctx.M0 = M0
         ctx.w_dtype = weight.dtype
+        ctx.b_dtype = None if bias is None else bias.dtype
         return y[:M0]
 
     @staticmethod
@@ -87,9 +91,13 @@ class _Float8LinearFn(torch.autograd.Function):
         dy8t = torch.empty((N, M), dtype=torch.uint8, device=dev)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        db = db_ws = None
+        if ctx.b_dtype is not None:
+            db = torch.empty((N,), dtype=torch.bfloat16, device=dev)
+            db_ws = f8lin.new_dbias_workspace(M, N, dev)
         f8lin.backward(dy, x8t, w8t, dx, dw, dy8, dy8t, f8lin.ScaleView(sx_scale), f8lin.ScaleView(sw_scale),
-                       layer.sdy, layer.ws, layer._mode("dy"), layer.config.amax_algo)
-        return dx[:ctx.M0], dw.to(ctx.w_dtype), None
+                       layer.sdy, layer.ws, layer._mode("dy"), layer.config.amax_algo, dbias=db, dbias_ws=db_ws)
+        return dx[:ctx.M0], dw.to(ctx.w_dtype), (None if db is None else db.to(ctx.b_dtype)), None
 
 
 class Float8Linear(nn.Module):
@@ -98,7 +106,7 @@ class Float8Linear(nn.Module):
     from the current amax (dynamic) or a 16-step amax history (delayed)."""
 
     def __init__(self, in_features: int, out_features: int, config: Optional[Float8LinearConfig] = None,
-                 weight: Optional[torch.Tensor] = None, device=None, dtype=torch.bfloat16):
+                 weight: Optional[torch.Tensor] = None, device=None, dtype=torch.bfloat16, bias=False):
         super().__init__()
         if in_features % 16 or out_features % 16:
             raise ValueError("Float8Linear needs in_features and out_features that are multiples of 16")
@@ -109,6 +117,15 @@ class Float8Linear(nn.Module):
             weight = torch.empty((out_features, in_features), device=device, dtype=dtype)
             nn.init.kaiming_uniform_(weight, a=5 ** 0.5)
         self.weight = weight if isinstance(weight, nn.Parameter) else nn.Parameter(weight)
+        # bias: False / True (a zero-initialised bias), or an existing tensor / Parameter to share
+        if isinstance(bias, torch.Tensor):
+            if tuple(bias.shape) != (out_features,):
+                raise ValueError("bias must have shape (out_features,)")
+            self.bias = bias if isinstance(bias, nn.Parameter) else nn.Parameter(bias)
+        elif bias:
+            self.bias = nn.Parameter(torch.zeros(out_features, device=self.weight.device, dtype=self.weight.dtype))
+        else:
+            self.register_parameter("bias", None)
         self._states_device = None
         self._initialized: Dict[str, bool] = {"x": False, "w": False, "dy": False}
 
@@ -149,30 +166,31 @@ class Float8Linear(nn.Module):
             raise ValueError(f"expected last dimension {self.in_features}, got {x.shape[-1]}")
         self._ensure_states(x.device)
         lead = x.shape[:-1]
-        y = _Float8LinearFn.apply(x.reshape(-1, self.in_features), self.weight, self)
+        y = _Float8LinearFn.apply(x.reshape(-1, self.in_features), self.weight, self.bias, self)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self):
         c = self.config
-        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+        return (f"in_features={self.in_features}, out_features={self.out_features}, bias={self.bias is not None}, "
                 f"input={c.cast_config_input.scaling_type}, weight={c.cast_config_weight.scaling_type}, "
                 f"grad_output={c.cast_config_grad_output.scaling_type}, amax_algo={c.amax_algo}")
 
 
 def convert_to_float8_training(module: nn.Module, config: Optional[Float8LinearConfig] = None,
                                module_filter_fn=None) -> nn.Module:
-    """Replaces every bias-free nn.Linear whose dimensions are multiples of 16
-    (and that module_filter_fn(fqn, module) accepts, if given) by a
-    Float8Linear sharing its weight Parameter.  Returns the module."""
+    """Replaces every nn.Linear whose dimensions are multiples of 16 (and that
+    module_filter_fn(fqn, module) accepts, if given) by a Float8Linear sharing
+    its weight and bias Parameters.  Returns the module."""
     config = config or Float8LinearConfig()
 
     def swap(parent: nn.Module, prefix: str):
         for name, child in list(parent.named_children()):
             fqn = f"{prefix}.{name}" if prefix else name
-            if (type(child) is nn.Linear and child.bias is None and child.in_features % 16 == 0
-                    and child.out_features % 16 == 0 and (module_filter_fn is None or module_filter_fn(fqn, child))):
+            if (type(child) is nn.Linear and child.in_features % 16 == 0 and child.out_features % 16 == 0
+                    and (module_filter_fn is None or module_filter_fn(fqn, child))):
                 setattr(parent, name, Float8Linear(child.in_features, child.out_features, config,
-                                                   weight=child.weight))
+                                                   weight=child.weight,
+                                                   bias=child.bias if child.bias is not None else False))
             else:
                 swap(child, fqn)
 

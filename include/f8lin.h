@@ -158,7 +158,10 @@ int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, 
  * Per tensor: amax (dynamic mode only), then one cast writing both layouts;
  * then Y = X8 . W8^T with the dequantisation epilogue.  x8t and w8t (and the
  * scales in sx, sw) are what backward needs; x8 and w8 can be reused or
- * freed after the call. */
+ * freed after the call.
+ * bias: optional (N) bf16 vector added to every row of Y in fp32 before the
+ * rounding to bf16 (the linear layers of pytorch/ao issue #1297's repro
+ * script keep nn.Linear's default bias); NULL for none.  16-byte aligned. */
 typedef struct {
   int64_t M, N, K;
   const uint16_t *x, *w; /* inputs */
@@ -170,13 +173,20 @@ typedef struct {
   int algo;           /* f8lin_amax_algo, for the dynamic-mode amax passes */
   void *ws;
   size_t ws_bytes;
+  const uint16_t *bias; /* (N) bf16, or NULL */
 } f8lin_fwd_args;
 
 /* Backward of the layer, given dY (M, N) bf16 and the forward's saved x8t,
  * w8t and scaling states: dY is cast once to e5m2 (both layouts), then
  * dX (M, K) = dY8 . W8 (contraction over N, B operand w8t) and
  * dW (N, K) = dY8^T . X8 (contraction over M, A operand dy8t, B operand x8t),
- * each with its dequantisation epilogue. */
+ * each with its dequantisation epilogue.
+ * dbias: optional (N) bf16 output, the bias gradient db[n] = sum over m of
+ * dY[m, n] (from the bf16 dY, summed in fp32 in a fixed order -- the same
+ * bits on every run -- and rounded once to bf16); NULL for none.  It needs
+ * dbias_ws, a scratch buffer of >= f8lin_dbias_workspace_bytes(M, N) bytes
+ * for the per-tile column sums (contents need no initialisation).  Both
+ * 16-byte aligned. */
 typedef struct {
   int64_t M, N, K;
   const uint16_t *dy;           /* input (M, N) */
@@ -188,7 +198,14 @@ typedef struct {
   int algo;                     /* f8lin_amax_algo */
   void *ws;
   size_t ws_bytes;
+  uint16_t *dbias;              /* (N) bf16 output, or NULL */
+  float *dbias_ws;              /* scratch for dbias, or NULL */
+  size_t dbias_ws_bytes;
 } f8lin_bwd_args;
+
+/* Bytes of dbias_ws that f8lin_backward needs for an (M, N) dY:
+ * max(1, ceil(M / 128)) * N * 4. */
+size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N);
 
 int f8lin_forward(const f8lin_fwd_args *args, void *stream);
 int f8lin_backward(const f8lin_bwd_args *args, void *stream);

@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_forward", "f8lin_backward",
                      "f8lin_delayed_update", "f8lin_gemm", "f8lin_gemm_batch", "f8lin_cast_f32", "f8lin_workspace_bytes",
+                     "f8lin_dbias_workspace_bytes",
                      "f8lin_status_str"):
         assert required in names
 
@@ -154,7 +155,46 @@ class Fwd(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)] + \
                [(n, ctypes.c_void_p) for n in ("x", "w", "y", "x8", "x8t", "w8", "w8t")] + \
                [("sx", State), ("sw", State), ("mode_x", ctypes.c_int), ("mode_w", ctypes.c_int),
-                ("algo", ctypes.c_int), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("algo", ctypes.c_int), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("bias", ctypes.c_void_p)]
+
+
+class Bwd(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)] + \
+               [(n, ctypes.c_void_p) for n in ("dy", "x8t", "w8t", "dx", "dw", "dy8", "dy8t")] + \
+               [("sx", State), ("sw", State), ("sdy", State), ("mode_dy", ctypes.c_int), ("algo", ctypes.c_int),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("dbias", ctypes.c_void_p),
+                ("dbias_ws", ctypes.c_void_p), ("dbias_ws_bytes", ctypes.c_size_t)]
+
+
+def test_backward_rejections(lib):
+    f = lib.f8lin_backward
+    f.argtypes = [ctypes.POINTER(Bwd), ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    g = lib.f8lin_dbias_workspace_bytes
+    g.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    g.restype = ctypes.c_size_t
+    assert g(300, 48) == 3 * 48 * 4 and g(0, 48) == 48 * 4 and g(128, 16) == 64
+    MB = 1 << 20
+    DB = A + 9 * MB
+    DBWS = A + 10 * MB
+
+    def args(**kw):
+        a = Bwd(288, 48, 64, A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB,
+                State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None),
+                State(AMAX + 128, SCALE + 128, None, None), 0, 0, WS, 8192, None, None, 0)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    need = g(288, 48)
+    assert f(None, None) == EINVAL
+    assert f(ctypes.byref(args(N=40)), None) == ESHAPE
+    assert f(ctypes.byref(args(dbias=DB)), None) == EWORKSPACE                          # dbias without scratch
+    assert f(ctypes.byref(args(dbias=DB, dbias_ws=DBWS, dbias_ws_bytes=need - 4)), None) == EWORKSPACE
+    assert f(ctypes.byref(args(dbias=DB + 2, dbias_ws=DBWS, dbias_ws_bytes=need)), None) == EALIGN
+    assert f(ctypes.byref(args(dbias=DB, dbias_ws=A, dbias_ws_bytes=need)), None) == EINVAL  # scratch is dY
+    assert f(ctypes.byref(args(dbias=A + MB, dbias_ws=DBWS, dbias_ws_bytes=need)), None) == EINVAL  # dbias in x8t
 
 
 def test_forward_rejections(lib):
@@ -178,6 +218,8 @@ def test_forward_rejections(lib):
     assert f(ctypes.byref(args(w8=A + 3 * MB)), None) == EINVAL  # w8 aliases x8
     assert f(ctypes.byref(args(sw=State(AMAX, SCALE + 64, None, None))), None) == EINVAL  # shared amax slot
     assert f(ctypes.byref(args(mode_x=1)), None) == EINVAL  # delayed without history
+    assert f(ctypes.byref(args(bias=A + 9 * MB + 2)), None) == EALIGN
+    assert f(ctypes.byref(args(bias=A + 2 * MB)), None) == EINVAL  # bias inside Y
 
 
 def test_delayed_update_rejections(lib):

@@ -89,3 +89,25 @@ def test_forward_twice_before_backward_uses_saved_scales(mod):
     ref = oracle.linear_step(bits(xa.detach()), bits(layer.weight.detach()), bits(dy))
     gemm_check(bf16_to_f64(ga), ref["dw"], what="micro-batch A dW")
     gemm_check(bf16_to_f64(xa.grad), ref["dx"], what="micro-batch A dX")
+
+
+def test_module_with_bias_matches_oracle(mod):
+    """A biased layer (the repro's nn.Linear layers keep their bias): Y
+    includes b, and bias.grad is the column sum of dY."""
+    from helpers import bf16_ulp
+    w = inputs.random_bf16((160, 96), seed=13, std=96 ** -0.5).to(DEV)
+    b = inputs.random_bf16((160,), seed=14, std=0.2).to(DEV)
+    layer = mod.Float8Linear(96, 160, weight=w, bias=b.clone())
+    x = inputs.random_bf16((3, 7, 96), seed=15).to(DEV).requires_grad_(True)  # 21 rows: padded to 32
+    dy = inputs.random_bf16((3, 7, 160), seed=16, std=1e-3 ** 0.5).to(DEV)
+    y = layer(x)
+    y.backward(dy)
+    torch.cuda.synchronize()
+    xb = _pad(bits(x.detach().reshape(21, 96)), 32)
+    dyb = _pad(bits(dy.reshape(21, 160)), 32)
+    ref = oracle.linear_step(xb, bits(layer.weight.detach()), dyb, bias_bits=bits(layer.bias.detach()))
+    gemm_check(bf16_to_f64(y.detach().reshape(21, 160)), ref["y"][:21], rms=float(np.sqrt(np.mean(ref["y"] ** 2))),
+               what="module Y + b")
+    got = bf16_to_f64(layer.bias.grad)
+    absum = np.abs(oracle.bf16_to_f64(dyb)).sum(axis=0)
+    assert np.all(np.abs(got - ref["dbias"]) <= 1e-5 * absum + bf16_ulp(ref["dbias"]))

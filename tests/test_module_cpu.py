@@ -13,8 +13,12 @@ def test_convert_swaps_only_eligible_linears():
     m.convert_to_float8_training(model)
     assert isinstance(model[0], m.Float8Linear) and model[0].weight is w0  # weight shared, not copied
     assert type(model[2]) is nn.Linear  # out_features not a multiple of 16
-    assert type(model[3]) is nn.Linear  # has a bias
+    assert type(model[3]) is nn.Linear  # in_features not a multiple of 16
     assert isinstance(model[4][0], m.Float8Linear)
+    model = nn.Sequential(nn.Linear(64, 128, bias=True))
+    b0 = model[0].bias
+    m.convert_to_float8_training(model)
+    assert isinstance(model[0], m.Float8Linear) and model[0].bias is b0  # bias shared too
 
 
 def test_convert_with_filter_and_bare_linear():
