@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_workspace_and_status_strings(lib):
     lib.f8lin_workspace_bytes.restype = ctypes.c_size_t
-    assert lib.f8lin_workspace_bytes() >= 4096
+    assert 4096 <= lib.f8lin_workspace_bytes() <= WSB
     lib.f8lin_status_str.restype = ctypes.c_char_p
     lib.f8lin_status_str.argtypes = [ctypes.c_int]
     for code in range(6):
@@ -69,6 +69,7 @@ AMAX = 0x50000000
 SCALE = 0x50000100
 HIST = 0x50000200
 META = 0x50000300
+WSB = 1 << 20  # a workspace size above f8lin_workspace_bytes()
 
 
 def test_amax_rejections(lib):
@@ -76,15 +77,15 @@ def test_amax_rejections(lib):
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_size_t, ctypes.c_void_p]
     f.restype = ctypes.c_int
-    assert f(A, 64, 0, None, WS, 8192, None) == EINVAL          # no output
-    assert f(None, 64, 0, AMAX, WS, 8192, None) == EINVAL       # no input with elements
-    assert f(A, 64, 2, AMAX, WS, 8192, None) == EINVAL          # bad algorithm
-    assert f(A, -1, 0, AMAX, WS, 8192, None) == ESHAPE
-    assert f(A + 2, 64, 0, AMAX, WS, 8192, None) == EALIGN
-    assert f(A, 64, 0, AMAX, None, 8192, None) == EWORKSPACE
+    assert f(A, 64, 0, None, WS, WSB, None) == EINVAL          # no output
+    assert f(None, 64, 0, AMAX, WS, WSB, None) == EINVAL       # no input with elements
+    assert f(A, 64, 2, AMAX, WS, WSB, None) == EINVAL          # bad algorithm
+    assert f(A, -1, 0, AMAX, WS, WSB, None) == ESHAPE
+    assert f(A + 2, 64, 0, AMAX, WS, WSB, None) == EALIGN
+    assert f(A, 64, 0, AMAX, None, WSB, None) == EWORKSPACE
     assert f(A, 64, 0, AMAX, WS, 16, None) == EWORKSPACE
-    assert f(A, 64, 1, AMAX, WS + 8, 8192, None) == EWORKSPACE   # misaligned workspace
-    assert f(A, 64, 0, A + 16, WS, 8192, None) == EINVAL       # output inside the input
+    assert f(A, 64, 1, AMAX, WS + 8, WSB, None) == EWORKSPACE   # misaligned workspace
+    assert f(A, 64, 0, A + 16, WS, WSB, None) == EINVAL       # output inside the input
 
 
 def test_cast_rejections(lib):
@@ -182,7 +183,7 @@ def test_backward_rejections(lib):
     def args(**kw):
         a = Bwd(288, 48, 64, A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB,
                 State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None),
-                State(AMAX + 128, SCALE + 128, None, None), 0, 0, WS, 8192, None, None, 0)
+                State(AMAX + 128, SCALE + 128, None, None), 0, 0, WS, WSB, None, None, 0)
         for k, v in kw.items():
             setattr(a, k, v)
         return a
@@ -205,7 +206,7 @@ def test_forward_rejections(lib):
 
     def args(**kw):
         a = Fwd(32, 48, 64, A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB,
-                State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None), 0, 0, 0, WS, 8192)
+                State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None), 0, 0, 0, WS, WSB)
         for k, v in kw.items():
             setattr(a, k, v)
         return a
