@@ -16,6 +16,8 @@
 #include <string.h>
 
 #include "device_common.h"
+#include <cstring>
+
 #include "internal.h"
 
 namespace f8lin {
@@ -128,6 +130,117 @@ int validate_gemm(const uint8_t *a, int fa, const uint8_t *b, int fb, int64_t M,
   return F8LIN_OK;
 }
 
+// Forward of `count` linears sharing X (count 1 is f8lin_forward): every
+// argument is checked before anything is launched; then amax + cast of X and
+// of each weight whose cast is not reused (two tensors of one scaling mode
+// per launch, each two-pass amax launch directly followed by the cast that
+// reduces its partials), then one GEMM launch for all of them.
+int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
+  if (!list || count < 1 || count > kMaxGemms) return F8LIN_EINVAL;
+  const f8lin_fwd_args &a0 = list[0];
+  F8_TRY(check_mode(a0.mode_x));
+  F8_TRY(check_algo(a0.algo));
+  F8_TRY(check_state(a0.sx, a0.mode_x));
+  if (bad_dim(a0.M) || bad_dim(a0.K) || a0.M * a0.K > kMaxElems) return F8LIN_ESHAPE;
+  const int64_t M = a0.M, K = a0.K, mk = M * K;
+  if (missing(a0.x, mk) || missing(a0.x8, mk) || missing(a0.x8t, mk)) return F8LIN_EINVAL;
+  if (!aligned16(a0.x) || !aligned16(a0.x8) || !aligned16(a0.x8t)) return F8LIN_EALIGN;
+  bool need_ws = a0.mode_x == F8LIN_DYNAMIC;
+  Range outs[4 + 5 * kMaxGemms + 1], ins[2 + 6 * kMaxGemms];
+  int no = 0, ni = 0;
+  outs[no++] = {a0.x8, mk};
+  outs[no++] = {a0.x8t, mk};
+  outs[no++] = {a0.sx.scale, 8};
+  outs[no++] = {a0.sx.amax, 4};
+  ins[ni++] = {a0.x, 2 * mk};
+  ins[ni++] = {a0.sx.history, a0.mode_x == F8LIN_DELAYED ? 64 : 0};
+  for (int i = 0; i < count; ++i) {
+    const f8lin_fwd_args &a = list[i];
+    if (i > 0 && (a.x != a0.x || a.x8 != a0.x8 || a.x8t != a0.x8t || a.M != M || a.K != K || a.mode_x != a0.mode_x ||
+                  a.algo != a0.algo || a.ws != a0.ws || a.ws_bytes != a0.ws_bytes ||
+                  std::memcmp(&a.sx, &a0.sx, sizeof(f8lin_state)) != 0))
+      return F8LIN_EINVAL;  // entries must share X, its copies, its state and the workspace
+    const bool reuse = a.w_cast_valid != 0;
+    if (reuse) {
+      if (!a.sw.scale) return F8LIN_EINVAL;
+    } else {
+      F8_TRY(check_mode(a.mode_w));
+      F8_TRY(check_state(a.sw, a.mode_w));
+    }
+    if (bad_dim(a.N) || a.N * K > kMaxElems || M * a.N > kMaxElems) return F8LIN_ESHAPE;
+    const int64_t nk = a.N * K, mn = M * a.N;
+    if ((!reuse && missing(a.w, nk)) || missing(a.w8, nk) || missing(a.w8t, nk) || missing(a.y, mn))
+      return F8LIN_EINVAL;
+    if ((!reuse && !aligned16(a.w)) || !aligned16(a.y) || !aligned16(a.w8) || !aligned16(a.w8t) ||
+        !aligned16(a.bias))
+      return F8LIN_EALIGN;
+    outs[no++] = {a.y, 2 * mn};
+    if (reuse) {
+      ins[ni++] = {a.w8, nk};
+      ins[ni++] = {a.w8t, nk};
+      ins[ni++] = {a.sw.scale, 8};
+    } else {
+      need_ws = need_ws || a.mode_w == F8LIN_DYNAMIC;
+      outs[no++] = {a.w8, nk};
+      outs[no++] = {a.w8t, nk};
+      outs[no++] = {a.sw.scale, 8};
+      outs[no++] = {a.sw.amax, 4};
+      ins[ni++] = {a.w, 2 * nk};
+      ins[ni++] = {a.sw.history, a.mode_w == F8LIN_DELAYED ? 64 : 0};
+    }
+    ins[ni++] = {a.bias, a.bias ? 2 * a.N : 0};
+  }
+  if (need_ws) {
+    F8_TRY(check_ws(a0.ws, a0.ws_bytes));
+    outs[no++] = {a0.ws, (int64_t)kWorkspaceBytes};
+  }
+  if (any_overlap(outs, no, ins, ni)) return F8LIN_EINVAL;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *ws = (uint32_t *)a0.ws;
+  // The tensors to cast, dynamic-mode ones first.
+  CastTensor ct[1 + kMaxGemms];
+  int modes[1 + kMaxGemms], nt = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int mode = pass == 0 ? F8LIN_DYNAMIC : F8LIN_DELAYED;
+    if (a0.mode_x == mode) {
+      ct[nt] = CastTensor{a0.x, M, K, &a0.sx, a0.x8, a0.x8t};
+      modes[nt++] = mode;
+    }
+    for (int i = 0; i < count; ++i) {
+      const f8lin_fwd_args &a = list[i];
+      if (!a.w_cast_valid && a.mode_w == mode) {
+        ct[nt] = CastTensor{a.w, a.N, K, &a.sw, a.w8, a.w8t};
+        modes[nt++] = mode;
+      }
+    }
+  }
+  for (int i = 0; i < nt;) {
+    const int n = (i + 1 < nt && modes[i + 1] == modes[i]) ? 2 : 1;
+    CastTensor pair[2] = {ct[i], n > 1 ? ct[i + 1] : ct[i]};
+    if (modes[i] == F8LIN_DYNAMIC) {
+      AmaxTensor am[2];
+      for (int j = 0; j < n; ++j) am[j] = AmaxTensor{pair[j].x, pair[j].rows * pair[j].cols, pair[j].st->amax};
+      if (a0.algo == F8LIN_AMAX_TWOPASS) {
+        const uint32_t *parts[2] = {nullptr, nullptr};
+        int nparts[2] = {0, 0};
+        F8_TRY(status_of(launch_amax_partials(am, n, ws, parts, nparts, s)));
+        for (int j = 0; j < n; ++j) pair[j].partials = parts[j], pair[j].npartials = nparts[j];
+      } else {
+        F8_TRY(status_of(launch_amax(am, n, a0.algo, ws, s)));
+      }
+    }
+    F8_TRY(status_of(launch_cast(pair, n, F8LIN_E4M3, modes[i], s)));
+    i += n;
+  }
+  GemmDesc g[kMaxGemms];
+  for (int i = 0; i < count; ++i) {
+    const f8lin_fwd_args &a = list[i];
+    g[i] = GemmDesc{a0.x8, a.w8, a0.sx.scale + 1, a.sw.scale + 1, a.y, M, a.N, K, a.bias};
+  }
+  return status_of(launch_gemms(g, count, F8LIN_E4M3, F8LIN_E4M3, s));
+}
+
 // Row tiles of the cast kernel: the number of per-tile column sums the bias
 // gradient reduces (one when dY has no rows: that tile's sums are zeros).
 int64_t dbias_tiles(int64_t M) { return M > 0 ? (M + kCastTile - 1) / kCastTile : 1; }
@@ -216,70 +329,10 @@ int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, 
   return status_of(launch_gemms(g, count, fmt_a, fmt_b, (hipStream_t)stream));
 }
 
-int f8lin_forward(const f8lin_fwd_args *p, void *stream) {
-  if (!p) return F8LIN_EINVAL;
-  const f8lin_fwd_args a = *p;
-  F8_TRY(check_mode(a.mode_x));
-  F8_TRY(check_mode(a.mode_w));
-  F8_TRY(check_algo(a.algo));
-  F8_TRY(check_state(a.sx, a.mode_x));
-  F8_TRY(check_state(a.sw, a.mode_w));
-  if (bad_dim(a.M) || bad_dim(a.N) || bad_dim(a.K) || a.M * a.K > kMaxElems || a.N * a.K > kMaxElems ||
-      a.M * a.N > kMaxElems)
-    return F8LIN_ESHAPE;
-  if (missing(a.x, a.M * a.K) || missing(a.x8, a.M * a.K) || missing(a.x8t, a.M * a.K) ||
-      missing(a.w, a.N * a.K) || missing(a.w8, a.N * a.K) || missing(a.w8t, a.N * a.K) || missing(a.y, a.M * a.N))
-    return F8LIN_EINVAL;
-  if (!aligned16(a.x) || !aligned16(a.w) || !aligned16(a.y) || !aligned16(a.x8) || !aligned16(a.x8t) ||
-      !aligned16(a.w8) || !aligned16(a.w8t) || !aligned16(a.bias))
-    return F8LIN_EALIGN;
-  const bool need_ws = a.mode_x == F8LIN_DYNAMIC || a.mode_w == F8LIN_DYNAMIC;
-  if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
-  const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
-  const Range outs[10] = {{a.y, 2 * mn},   {a.x8, mk},   {a.x8t, mk},
-                          {a.w8, nk},      {a.w8t, nk},  {a.sx.scale, 8},
-                          {a.sw.scale, 8}, {a.sx.amax, 4}, {a.sw.amax, 4},
-                          {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0}};
-  const Range ins[5] = {{a.x, 2 * mk},
-                        {a.w, 2 * nk},
-                        {a.sx.history, a.mode_x == F8LIN_DELAYED ? 64 : 0},
-                        {a.sw.history, a.mode_w == F8LIN_DELAYED ? 64 : 0},
-                        {a.bias, a.bias ? 2 * a.N : 0}};
-  if (any_overlap(outs, 10, ins, 5)) return F8LIN_EINVAL;
+int f8lin_forward(const f8lin_fwd_args *p, void *stream) { return forward_impl(p, 1, stream); }
 
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t *ws = (uint32_t *)a.ws;
-  // One amax launch for every dynamic-mode tensor, one cast launch for both
-  // tensors when they share a scaling mode.  The two-pass amax leaves its
-  // partial maxima for the cast's prologue to reduce.
-  AmaxTensor am[2];
-  int na = 0;
-  if (a.mode_x == F8LIN_DYNAMIC) am[na++] = AmaxTensor{a.x, mk, a.sx.amax};
-  if (a.mode_w == F8LIN_DYNAMIC) am[na++] = AmaxTensor{a.w, nk, a.sw.amax};
-  const uint32_t *parts[2] = {nullptr, nullptr};
-  int nparts[2] = {0, 0};
-  if (na > 0) {
-    if (a.algo == F8LIN_AMAX_TWOPASS)
-      F8_TRY(status_of(launch_amax_partials(am, na, ws, parts, nparts, s)));
-    else
-      F8_TRY(status_of(launch_amax(am, na, a.algo, ws, s)));
-  }
-  CastTensor cx = {a.x, a.M, a.K, &a.sx, a.x8, a.x8t};
-  CastTensor cw = {a.w, a.N, a.K, &a.sw, a.w8, a.w8t};
-  {
-    int i = 0;
-    if (a.mode_x == F8LIN_DYNAMIC) cx.partials = parts[i], cx.npartials = nparts[i], ++i;
-    if (a.mode_w == F8LIN_DYNAMIC) cw.partials = parts[i], cw.npartials = nparts[i], ++i;
-  }
-  if (a.mode_x == a.mode_w) {
-    const CastTensor both[2] = {cx, cw};
-    F8_TRY(status_of(launch_cast(both, 2, F8LIN_E4M3, a.mode_x, s)));
-  } else {
-    F8_TRY(status_of(launch_cast(&cx, 1, F8LIN_E4M3, a.mode_x, s)));
-    F8_TRY(status_of(launch_cast(&cw, 1, F8LIN_E4M3, a.mode_w, s)));
-  }
-  const GemmDesc g = {a.x8, a.w8, a.sx.scale + 1, a.sw.scale + 1, a.y, a.M, a.N, a.K, a.bias};
-  return status_of(launch_gemms(&g, 1, F8LIN_E4M3, F8LIN_E4M3, s));
+int f8lin_forward_shared_x(const f8lin_fwd_args *args, int count, void *stream) {
+  return forward_impl(args, count, stream);
 }
 
 int f8lin_backward(const f8lin_bwd_args *p, void *stream) {

@@ -4,9 +4,9 @@
 //   C (M, N) bf16 = (A (M, K) . B (N, K)^T) * inv_a * inv_b
 // Both operands are K-contiguous ("TN"); the cast kernel writes the
 // transposed fp8 copies so that forward, dgrad and wgrad all take this form.
-// One launch runs a list of up to two such problems (the backward's dgrad
-// and wgrad go together); problems with M <= 64 take a skinny kernel of
-// their own (below).
+// One launch runs a list of up to four such problems (the backward's dgrad
+// and wgrad go together, so do the forwards of linears that share their
+// input); problems with M <= 64 take a skinny kernel of their own (below).
 //
 // gfx950 design (each choice measured on MI355X):
 //   * v_mfma_f32_32x32x64_f8f6f4 (the scaled builtin with zero scale operands
@@ -138,8 +138,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   }
 
   for (int it = local_wg; it < total; it += wx) {
-    const int pi = it < len[0] ? 0 : 1;
-    const int t = start[pi] + (pi ? it - len[0] : it);
+    // problem pi, tile t of it: this XCD's shares of the problems follow one another
+    int pi = 0, off = it;
+#pragma unroll
+    for (int i = 0; i + 1 < kMaxGemms; ++i)
+      if (pi == i && off >= len[i]) {
+        off -= len[i];
+        pi = i + 1;
+      }
+    const int t = start[pi] + off;
     const Problem P = batch.p[pi];
     const int M = P.M, N = P.N, K = P.K;
     int tm, tn;

@@ -57,8 +57,8 @@ hipError_t launch_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b,
                        int64_t K, const float *inv_a, const float *inv_b, uint16_t *c, hipStream_t stream);
 
 // Up to kMaxGemms GEMMs with the same operand formats in one persistent
-// launch (the backward's dgrad and wgrad).
-constexpr int kMaxGemms = 2;
+// launch (the backward's dgrad and wgrad; forwards sharing their input).
+constexpr int kMaxGemms = 4;
 struct GemmDesc {
   const uint8_t *a, *b;
   const float *inv_a, *inv_b;

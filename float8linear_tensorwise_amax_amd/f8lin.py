@@ -47,14 +47,14 @@ class GemmDesc(ctypes.Structure):
                 ("M", _i64), ("N", _i64), ("K", _i64)]
 
 
-MAX_BATCH = 2
+MAX_BATCH = 4
 
 
 class FwdArgs(ctypes.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("x", _vp), ("w", _vp), ("y", _vp),
                 ("x8", _vp), ("x8t", _vp), ("w8", _vp), ("w8t", _vp), ("sx", State), ("sw", State),
                 ("mode_x", _int), ("mode_w", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
-                ("bias", _vp)]
+                ("bias", _vp), ("w_cast_valid", _int)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -76,6 +76,7 @@ _lib.f8lin_cast_f32.argtypes = [_vp, _i64, _int, _vp, _vp]
 _lib.f8lin_gemm.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
 _lib.f8lin_gemm_batch.argtypes = [ctypes.POINTER(GemmDesc), _int, _int, _int, _vp]
 _lib.f8lin_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+_lib.f8lin_forward_shared_x.argtypes = [ctypes.POINTER(FwdArgs), _int, _vp]
 _lib.f8lin_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp]
 _lib.f8lin_delayed_update.argtypes = [ctypes.POINTER(State), _int, _vp]
 for _name in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_cast_f32", "f8lin_gemm", "f8lin_forward",
@@ -222,19 +223,37 @@ def gemm_batch(items, fmt_a, fmt_b, stream=None):
     _check(_lib.f8lin_gemm_batch(arr, len(items), _FMT[fmt_a], _FMT[fmt_b], _stream(stream)))
 
 
-def forward(x, w, y, x8, x8t, w8, w8t, sx: ScalingState, sw: ScalingState, ws, mode_x="dynamic",
-            mode_w="dynamic", algo="atomic", stream=None, bias=None):
+def _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias, w_cast_valid):
     M, K = x.shape
-    N = w.shape[0]
+    N = w8.shape[0]
+    if (w is not None and tuple(w.shape) != (N, K)) or tuple(w8.shape) != (N, K) or tuple(y.shape) != (M, N):
+        raise ValueError("forward: shape mismatch")
     if bias is not None and tuple(bias.shape) != (N,):
         raise ValueError("forward: bias must have shape (N,)")
-    a = FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
-                _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
-                sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
-                ws.numel() * ws.element_size(), None if bias is None else _ptr(bias, torch.bfloat16))
-    if w.shape[1] != K or tuple(y.shape) != (M, N):
-        raise ValueError("forward: shape mismatch")
+    return FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
+                   _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
+                   sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
+                   ws.numel() * ws.element_size(), None if bias is None else _ptr(bias, torch.bfloat16),
+                   1 if w_cast_valid else 0)
+
+
+def forward(x, w, y, x8, x8t, w8, w8t, sx: ScalingState, sw: ScalingState, ws, mode_x="dynamic",
+            mode_w="dynamic", algo="atomic", stream=None, bias=None, w_cast_valid=False):
+    """w_cast_valid: w8, w8t and sw's scale already hold W's cast (unchanged
+    weight); W's amax and cast are skipped and w may be None."""
+    a = _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias, w_cast_valid)
     _check(_lib.f8lin_forward(ctypes.byref(a), _stream(stream)))
+
+
+def forward_shared_x(x, x8, x8t, sx: ScalingState, ws, linears, mode_x="dynamic", algo="atomic", stream=None):
+    """Linears reading the same X: linears is a list of dicts with keys w, y,
+    w8, w8t, sw and optionally mode_w, bias, w_cast_valid.  X is cast once;
+    the GEMMs share one launch."""
+    arr = (FwdArgs * max(1, len(linears)))()
+    for i, l in enumerate(linears):
+        arr[i] = _fwd_args(x, l.get("w"), l["y"], x8, x8t, l["w8"], l["w8t"], sx, l["sw"], ws, mode_x,
+                           l.get("mode_w", "dynamic"), algo, l.get("bias"), l.get("w_cast_valid", False))
+    _check(_lib.f8lin_forward_shared_x(arr, len(linears), _stream(stream)))
 
 
 def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState, sdy: ScalingState, ws,

@@ -145,7 +145,7 @@ int f8lin_gemm(const uint8_t *a, int fmt_a, const uint8_t *b, int fmt_b, int64_t
  * Errors: as f8lin_gemm for each entry; an output overlapping any other
  * entry's input or output is F8LIN_EINVAL; nothing is launched unless every
  * entry is valid. */
-#define F8LIN_MAX_BATCH 2
+#define F8LIN_MAX_BATCH 4
 typedef struct {
   const uint8_t *a, *b;                      /* (M, K), (N, K) fp8 codes, K-contiguous */
   const float *inv_scale_a, *inv_scale_b;    /* [1] each */
@@ -174,6 +174,11 @@ typedef struct {
   void *ws;
   size_t ws_bytes;
   const uint16_t *bias; /* (N) bf16, or NULL */
+  /* Nonzero: w8, w8t and sw.scale already hold the cast of this W from an
+   * earlier forward (the weight is unchanged, e.g. between the micro-batches
+   * of one optimizer step), so W's amax and cast are skipped and w is not
+   * read. */
+  int w_cast_valid;
 } f8lin_fwd_args;
 
 /* Backward of the layer, given dY (M, N) bf16 and the forward's saved x8t,
@@ -208,6 +213,18 @@ typedef struct {
 size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N);
 
 int f8lin_forward(const f8lin_fwd_args *args, void *stream);
+
+/* Forward of count (1 .. F8LIN_MAX_BATCH) linears that read the same input X,
+ * such as the q, k and v projections of an attention block or the two input
+ * projections of a gated MLP: X is cast once (amax, scale, X8, X8^T), each
+ * weight as in f8lin_forward, and the count GEMMs run in one launch.  Every
+ * entry gives the same M, K, x, x8, x8t, sx, mode_x, algo and workspace;
+ * N, w, y, w8, w8t, sw, mode_w, bias and w_cast_valid are per entry.  Each
+ * output equals, bit for bit, what f8lin_forward gives for that entry.
+ * Errors: as f8lin_forward for each entry; entries that disagree on the
+ * shared fields, or outputs that overlap any entry's input or output, are
+ * F8LIN_EINVAL; nothing is launched unless every entry is valid. */
+int f8lin_forward_shared_x(const f8lin_fwd_args *args, int count, void *stream);
 int f8lin_backward(const f8lin_bwd_args *args, void *stream);
 
 /* After backward (the sync step of delayed scaling), for each of the

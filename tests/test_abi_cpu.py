@@ -137,10 +137,11 @@ def test_gemm_batch_rejections(lib):
     C2 = C + (1 << 20)
     ok0 = GemmDesc(A, B, AMAX, SCALE, C, 32, 48, 64)
     ok1 = GemmDesc(B, A, AMAX, SCALE, C2, 48, 32, 64)
-    arr = (GemmDesc * 3)(ok0, ok1, ok0)
+    arr = (GemmDesc * 5)(ok0, ok1, ok0, ok1, ok0)
     assert f(None, 1, 0, 0, None) == EINVAL
     assert f(arr, 0, 0, 0, None) == EINVAL                      # empty batch
-    assert f(arr, 3, 0, 0, None) == EINVAL                      # more than F8LIN_MAX_BATCH
+    assert f(arr, 5, 0, 0, None) == EINVAL                      # more than F8LIN_MAX_BATCH
+    assert f(arr, 3, 0, 0, None) == EINVAL                      # entries 0 and 2 write the same C
     assert f(arr, 2, 0, 4, None) == EINVAL                      # bad format
     bad = (GemmDesc * 2)(ok0, GemmDesc(B, A, AMAX, SCALE, C2, 48, 32, 65))
     assert f(bad, 2, 0, 0, None) == ESHAPE                      # second entry's K not a multiple of 16
@@ -157,7 +158,7 @@ class Fwd(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in ("x", "w", "y", "x8", "x8t", "w8", "w8t")] + \
                [("sx", State), ("sw", State), ("mode_x", ctypes.c_int), ("mode_w", ctypes.c_int),
                 ("algo", ctypes.c_int), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
-                ("bias", ctypes.c_void_p)]
+                ("bias", ctypes.c_void_p), ("w_cast_valid", ctypes.c_int)]
 
 
 class Bwd(ctypes.Structure):
@@ -221,6 +222,23 @@ def test_forward_rejections(lib):
     assert f(ctypes.byref(args(mode_x=1)), None) == EINVAL  # delayed without history
     assert f(ctypes.byref(args(bias=A + 9 * MB + 2)), None) == EALIGN
     assert f(ctypes.byref(args(bias=A + 2 * MB)), None) == EINVAL  # bias inside Y
+    # a reused weight cast: w is not read (null allowed), but w8 / w8t / scale must be there
+    assert f(ctypes.byref(args(w_cast_valid=1, w=None, sw=State(AMAX + 64, None, None, None))), None) == EINVAL
+    assert f(ctypes.byref(args(w_cast_valid=1, w=None, w8=None)), None) == EINVAL
+    # shared X: every entry must agree on X and its state
+    g = lib.f8lin_forward_shared_x
+    g.argtypes = [ctypes.POINTER(Fwd), ctypes.c_int, ctypes.c_void_p]
+    g.restype = ctypes.c_int
+    e1 = args(w=A + 7 * MB, y=A + 8 * MB, w8=A + 9 * MB, w8t=A + 10 * MB, sw=State(AMAX + 128, SCALE + 128, None, None))
+    pair = (Fwd * 2)(args(), e1)
+    assert g(pair, 0, None) == EINVAL
+    assert g(pair, 5, None) == EINVAL
+    bad = (Fwd * 2)(args(), args(w=A + 7 * MB, y=A + 8 * MB, w8=A + 9 * MB, w8t=A + 10 * MB, x=A + 11 * MB,
+                                 sw=State(AMAX + 128, SCALE + 128, None, None)))
+    assert g(bad, 2, None) == EINVAL                                  # different X
+    clash = (Fwd * 2)(args(), args(w=A + 7 * MB, w8=A + 9 * MB, w8t=A + 10 * MB,
+                                   sw=State(AMAX + 128, SCALE + 128, None, None)))
+    assert g(clash, 2, None) == EINVAL                                # both write the same Y
 
 
 def test_delayed_update_rejections(lib):

@@ -233,8 +233,8 @@ def test_empty_token_dimension(f8):
 
 
 def test_rejected_call_writes_nothing(f8):
-    buf = f8.LinearBuffers(32, 48, 64, DEV)
-    x = inputs.random_bf16((32, 64), seed=1).to(DEV)
+    buf = f8.LinearBuffers(48, 48, 64, DEV)  # M = N, so x8 has w8's shape and only the aliasing is wrong
+    x = inputs.random_bf16((48, 64), seed=1).to(DEV)
     w = inputs.random_bf16((48, 64), seed=2).to(DEV)
     buf.y.fill_(3.0)
     with pytest.raises(f8.F8linError):
