@@ -22,6 +22,9 @@ Workload shapes follow the pages:
   * a GPT-1.5B block at batch 12 x seq 1024 (pytorch/ao issue #1297, repro
     script: d_embd 1600, attn_proj 3*d, out_proj d, FFN 4*d), delayed
     scaling, a fresh seed per step.
+A workload may name groups of linears that read one input (the q, k, v
+projections, the gated MLP's w1 and w3): only the group's first linear
+draws X; the others reuse it and draw only W and dY.
 """
 from dataclasses import dataclass
 from typing import List, Tuple
@@ -55,6 +58,7 @@ class Workload:
     outlier_multiplier: float = 200.0
     seed: int = 0
     description: str = ""
+    shared_x: Tuple[Tuple[str, ...], ...] = ()  # groups of linears reading the same X
 
     @property
     def flops(self) -> int:
@@ -84,6 +88,9 @@ WORKLOADS = {
         description="single 4096->4096 linear, 65536 input rows, 0.1% of X scaled x200, dynamic"),
     "llama3_8b_layer_t8192": Workload("llama3_8b_layer_t8192", _llama_layer(8192),
                                       description="Llama-3-8B layer linears (q,k,v,o,w1,w3,w2), 8192 tokens"),
+    "llama3_8b_layer_t8192_shared": Workload(
+        "llama3_8b_layer_t8192_shared", _llama_layer(8192), shared_x=(("q", "k", "v"), ("w1", "w3")),
+        description="Llama-3-8B layer linears, 8192 tokens; q,k,v and w1,w3 read one input each (cast once)"),
     "gpt1p5b_block_t12288_delayed": Workload(
         "gpt1p5b_block_t12288_delayed", _gpt_block(12288), scaling="delayed", steps=20,
         description="GPT-1.5B block linears (qkv,out,fc1,fc2), 12288 tokens, delayed scaling, 20 steps"),
@@ -91,14 +98,16 @@ WORKLOADS = {
 
 
 def draw_linear(gen: torch.Generator, lin: Linear, outlier_fraction: float = 0.0,
-                outlier_multiplier: float = 200.0):
-    """Draws (X, W, dY) as bf16 CPU tensors, in that order, from `gen`."""
-    x = torch.randn((lin.M, lin.K), generator=gen, dtype=torch.float32) * X_STD
-    if outlier_fraction > 0.0:
-        mask = torch.rand((lin.M, lin.K), generator=gen, dtype=torch.float32) < outlier_fraction
-        x[mask] *= outlier_multiplier
-        del mask
-    x = x.to(torch.bfloat16)
+                outlier_multiplier: float = 200.0, x: torch.Tensor = None):
+    """Draws (X, W, dY) as bf16 CPU tensors, in that order, from `gen`; a
+    given x is used as is (nothing drawn for it)."""
+    if x is None:
+        x = torch.randn((lin.M, lin.K), generator=gen, dtype=torch.float32) * X_STD
+        if outlier_fraction > 0.0:
+            mask = torch.rand((lin.M, lin.K), generator=gen, dtype=torch.float32) < outlier_fraction
+            x[mask] *= outlier_multiplier
+            del mask
+        x = x.to(torch.bfloat16)
     w = (torch.randn((lin.N, lin.K), generator=gen, dtype=torch.float32) * (1.0 / lin.K ** 0.5)).to(torch.bfloat16)
     dy = (torch.randn((lin.M, lin.N), generator=gen, dtype=torch.float32) * DY_STD).to(torch.bfloat16)
     return x, w, dy
@@ -111,10 +120,31 @@ def workload_inputs(wl: Workload, step: int = 0) -> List[Tuple[Linear, torch.Ten
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     out = []
+    lead_x = {}
     for lin in wl.linears:
-        x, w, dy = draw_linear(gen, lin, wl.outlier_fraction, wl.outlier_multiplier)
+        group = next((g for g in wl.shared_x if lin.name in g), None)
+        shared = lead_x.get(group) if group else None
+        x, w, dy = draw_linear(gen, lin, wl.outlier_fraction, wl.outlier_multiplier, x=shared)
+        if group and shared is None:
+            lead_x[group] = x
         out.append((lin, x, w, dy))
     return out
+
+
+def groups_of(wl: Workload):
+    """Indices of wl.linears, grouped: one group per shared input (in order of
+    first appearance), singletons otherwise."""
+    groups, seen = [], {}
+    for i, lin in enumerate(wl.linears):
+        g = next((g for g in wl.shared_x if lin.name in g), None)
+        if g is None:
+            groups.append([i])
+        elif g in seen:
+            groups[seen[g]].append(i)
+        else:
+            seen[g] = len(groups)
+            groups.append([i])
+    return groups
 
 
 def random_bf16(shape, seed: int, std: float = 1.0) -> torch.Tensor:

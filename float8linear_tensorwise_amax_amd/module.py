@@ -40,6 +40,9 @@ class Float8LinearConfig:
     cast_config_weight: CastConfig = field(default_factory=CastConfig)
     cast_config_grad_output: CastConfig = field(default_factory=CastConfig)
     amax_algo: str = "twopass"  # "atomic" or "twopass"
+    # Reuse the weight's fp8 copies while the weight is unchanged (same tensor,
+    # same version counter: e.g. the micro-batches of one optimizer step).
+    reuse_weight_cast: bool = True
 
 
 def _pad_rows(t: torch.Tensor) -> torch.Tensor:
@@ -63,13 +66,24 @@ class _Float8LinearFn(torch.autograd.Function):
         u8 = dict(dtype=torch.uint8, device=dev)
         x8 = torch.empty((M, K), **u8)
         x8t = torch.empty((K, M), **u8)
-        w8 = torch.empty((N, K), **u8)
-        w8t = torch.empty((K, N), **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         mode_x = layer._mode("x")
         mode_w = layer._mode("w")
-        f8lin.forward(x, w, y, x8, x8t, w8, w8t, layer.sx, layer.sw, layer.ws, mode_x, mode_w,
-                      layer.config.amax_algo, bias=b)
+        key = (weight.data_ptr(), weight._version, weight.dtype, str(dev), mode_w)
+        cached = layer._w_cache if (layer.config.reuse_weight_cast and layer._w_cache is not None
+                                    and layer._w_cache[0] == key) else None
+        if cached is not None:
+            # unchanged weight: its fp8 copies and scale (in layer.sw) are still valid
+            w8, w8t = cached[1], cached[2]
+            layer.weight_cast_reuses += 1
+        else:
+            # fresh copies: an earlier forward's backward may still read the old ones
+            w8 = torch.empty((N, K), **u8)
+            w8t = torch.empty((K, N), **u8)
+        f8lin.forward(x, None if cached is not None else w, y, x8, x8t, w8, w8t, layer.sx, layer.sw, layer.ws,
+                      mode_x, mode_w, layer.config.amax_algo, bias=b, w_cast_valid=cached is not None)
+        if cached is None and layer.config.reuse_weight_cast:
+            layer._w_cache = (key, w8, w8t)
         # backward must use the scales these fp8 copies were made with, even if
         # the layer runs forward again before it (micro-batches, recomputation)
         ctx.save_for_backward(x8t, w8t, layer.sx.scale.clone(), layer.sw.scale.clone())
@@ -128,6 +142,8 @@ class Float8Linear(nn.Module):
             self.register_parameter("bias", None)
         self._states_device = None
         self._initialized: Dict[str, bool] = {"x": False, "w": False, "dy": False}
+        self._w_cache = None  # (key, w8, w8t) of the weight's last cast
+        self.weight_cast_reuses = 0
 
     # ---- scaling state (device-resident, created on first use on the weight's device)
     def _ensure_states(self, device):
@@ -138,6 +154,7 @@ class Float8Linear(nn.Module):
             self.ws = f8lin.new_workspace(device)
             self._states_device = device
             self._initialized = {"x": False, "w": False, "dy": False}
+            self._w_cache = None
 
     def _cfg(self, role):
         return {"x": self.config.cast_config_input, "w": self.config.cast_config_weight,
@@ -158,6 +175,8 @@ class Float8Linear(nn.Module):
         for role in ("x", "w", "dy"):
             if self._cfg(role).scaling_type == "delayed":
                 self._initialized[role] = True
+        if self._cfg("w").scaling_type == "delayed":
+            self._w_cache = None  # the history moved: the weight's scale changes
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if not x.is_cuda:

@@ -111,3 +111,30 @@ def test_module_with_bias_matches_oracle(mod):
     got = bf16_to_f64(layer.bias.grad)
     absum = np.abs(oracle.bf16_to_f64(dyb)).sum(axis=0)
     assert np.all(np.abs(got - ref["dbias"]) <= 1e-5 * absum + bf16_ulp(ref["dbias"]))
+
+
+def test_module_reuses_the_weight_cast_between_micro_batches(mod):
+    """Micro-batches before an optimizer step reuse the weight's fp8 copies
+    (same bits as recasting); an in-place update of the weight recasts it."""
+    torch.manual_seed(3)
+    w = inputs.random_bf16((128, 64), seed=31, std=0.125).to(DEV)
+    layer = mod.Float8Linear(64, 128, weight=w.clone())
+    fresh = mod.Float8Linear(64, 128, weight=w.clone(), config=mod.Float8LinearConfig(reuse_weight_cast=False))
+    xs = [inputs.random_bf16((32, 64), seed=32 + i).to(DEV) for i in range(3)]
+    dy = inputs.random_bf16((32, 128), seed=40, std=0.03).to(DEV)
+    for i, x in enumerate(xs):
+        y = layer(x)
+        y.backward(dy)
+        y2 = fresh(x)
+        y2.backward(dy)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), i
+    assert layer.weight_cast_reuses == 2 and fresh.weight_cast_reuses == 0
+    assert torch.equal(layer.weight.grad.view(torch.int16), fresh.weight.grad.view(torch.int16))
+    with torch.no_grad():
+        layer.weight.mul_(2.0)  # in place: the version counter moves
+        fresh.weight.mul_(2.0)
+    y, y2 = layer(xs[0]), fresh(xs[0])
+    torch.cuda.synchronize()
+    assert layer.weight_cast_reuses == 2
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
