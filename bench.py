@@ -163,8 +163,21 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t_host0
 
+    def step_spread(algo, n=100):
+        """Per-step HIP events around n further steps: median and min (the
+        events themselves add a little time per step)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for t, (a, b) in enumerate(evs):
+            a.record(stream)
+            step(args.warmup + args.steps + t, algo)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return ts[len(ts) // 2], ts[0]
+
     # ---- timed region (the headline), then the same with the other amax algorithm
     ms_per_step, t_host = timed_steps(args.algo)
+    ms_median, ms_min = step_spread(args.algo)
     other = "twopass" if args.algo == "atomic" else "atomic"
     ms_other = None if (delayed or args.only_timed) else timed_steps(other)[0]
     flops = wl.flops
@@ -190,6 +203,8 @@ def main():
                    "scaling": wl.scaling, "amax_algo": args.algo, "rotating_input_sets": R,
                    "inputs": "X~N(0,1), W~N(0,1/K), dY~N(0,1e-3) bf16, seeded"},
         "fwd_bwd_us": round(ms_per_step * 1e3, 2),
+        "fwd_bwd_us_per_step_events": {"median": round(ms_median * 1e3, 2), "min": round(ms_min * 1e3, 2),
+                                       "steps": 100},
         "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
         "host_wall_s_timed": round(t_host, 4),
     }
@@ -219,11 +234,14 @@ def main():
 
 
 def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
-    """Per-kernel durations: the same launch sequence as f8lin_forward /
-    f8lin_backward, issued entry point by entry point with HIP events between
-    the calls on the launch stream."""
-    acc = {"amax": [0.0, 0, 0.0], "cast": [0.0, 0, 0.0], "gemm_fwd": [0.0, 0, 0.0],
-           "gemm_bwd_pair": [0.0, 0, 0.0]}  # ms, launches, units
+    """Per-call and per-kernel durations with HIP events on the launch stream:
+    each f8lin_forward / f8lin_backward call as the step issues it, and its
+    GEMM launch again on its own (f8lin_gemm; f8lin_gemm_batch for the
+    backward's dgrad + wgrad pair).  A call's time minus its GEMM's is its
+    amax + cast phase, whose algorithmic bytes are 2 B/element for each
+    dynamic-mode amax pass and 4 B/element for each cast."""
+    acc = {k: [0.0, 0, 0.0] for k in ("fwd_call", "bwd_call", "gemm_fwd", "gemm_bwd_pair")}  # ms, calls, units
+    ew_bytes = {"fwd": 0, "bwd": 0}
     gemm_bytes = {"gemm_fwd": [], "gemm_bwd_pair": []}
 
     def timed(kind, fn, units):
@@ -234,22 +252,20 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
         b.record(stream)
         pending.append((kind, a, b, units))
 
-    # the timed loops ran just before, so the device is warm: fewer rounds suffice
+    # the timed loops ran just before, so the device is warm: fewer rounds
+    # suffice.  Everything is queued before one synchronisation, so the host
+    # stays ahead of the GPU and no call starts from an idle device.
     warm, steps = min(args.warmup, 10), min(args.steps, 100)
+    recorded = []
     for t in range(warm + steps):
         pending = []
         mode = "delayed" if (delayed and t > 0) else "dynamic"
         for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
-            if mode == "dynamic":
-                timed("amax", lambda: f8lin.amax(x, buf.sx.amax, buf.ws, args.algo), x.numel())
-                timed("amax", lambda: f8lin.amax(w, buf.sw.amax, buf.ws, args.algo), w.numel())
-            timed("cast", lambda: f8lin.cast_transpose(x, "e4m3", mode, buf.sx, buf.x8, buf.x8t), x.numel())
-            timed("cast", lambda: f8lin.cast_transpose(w, "e4m3", mode, buf.sw, buf.w8, buf.w8t), w.numel())
+            per = 6 if mode == "dynamic" else 4  # amax pass (dynamic) + cast
+            timed("fwd_call", lambda: buf.forward(x, w, mode, args.algo), per * (l.M * l.K + l.N * l.K))
             timed("gemm_fwd", lambda: f8lin.gemm(buf.x8, "e4m3", buf.w8, "e4m3", buf.sx.inv_scale,
                                                  buf.sw.inv_scale, buf.y), 2 * l.M * l.N * l.K)
-            if mode == "dynamic":
-                timed("amax", lambda: f8lin.amax(dy, buf.sdy.amax, buf.ws, args.algo), dy.numel())
-            timed("cast", lambda: f8lin.cast_transpose(dy, "e5m2", mode, buf.sdy, buf.dy8, buf.dy8t), dy.numel())
+            timed("bwd_call", lambda: buf.backward(dy, mode, args.algo), per * l.M * l.N)
             # dgrad and wgrad in one launch, as f8lin_backward issues them
             timed("gemm_bwd_pair", lambda: f8lin.gemm_batch(
                 [(buf.dy8, buf.w8t, buf.sdy.inv_scale, buf.sw.inv_scale, buf.dx),
@@ -261,12 +277,13 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                 gemm_bytes["gemm_fwd"].append(l.M * l.K + l.N * l.K + 2 * l.M * l.N)
                 gemm_bytes["gemm_bwd_pair"].append(l.M * l.N + l.N * l.K + 2 * l.M * l.K +
                                                    l.M * l.N + l.M * l.K + 2 * l.N * l.K)
-        torch.cuda.synchronize()
         if t >= warm:
-            for kind, a, b, units in pending:
-                acc[kind][0] += a.elapsed_time(b)
-                acc[kind][1] += 1
-                acc[kind][2] += units
+            recorded.extend(pending)
+    torch.cuda.synchronize()
+    for kind, a, b, units in recorded:
+        acc[kind][0] += a.elapsed_time(b)
+        acc[kind][1] += 1
+        acc[kind][2] += units
     k = {}
     for name in ("gemm_fwd", "gemm_bwd_pair"):
         ms, n, el = acc[name]
@@ -274,14 +291,20 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                    "tflops": round(el / (ms * 1e-3) / 1e12, 2),
                    "algorithmic_bytes_per_launch": int(sum(gemm_bytes[name]) / len(gemm_bytes[name])),
                    "flops_per_launch": int(el / n)}
-    ms, n, el = acc["cast"]
-    k["cast_transpose"] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
-                           "gbs": round(4 * el / (ms * 1e-3) / 1e9, 1),
-                           "frac_hbm_peak": round(4 * el / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                           "bytes_per_elem": 4}
+    for side, gemm in (("fwd", "gemm_fwd"), ("bwd", "gemm_bwd_pair")):
+        ms_call, n, by = acc[side + "_call"]
+        ms_ew = ms_call - acc[gemm][0]
+        k["amax_cast_" + side] = {"avg_us": round(ms_ew / n * 1e3, 3), "calls": n,
+                                  "call_avg_us": round(ms_call / n * 1e3, 3),
+                                  "gbs": round(by / (ms_ew * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(by / (ms_ew * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                  "algorithmic_bytes_per_call": int(by / n),
+                                  "what": ("amax pass(es) + cast of X and W" if side == "fwd" else
+                                           "amax pass + cast of dY") + " = call time minus its GEMM launch"}
     # amax alone, both algorithms, on the step's three tensors
     for algo in ("atomic", "twopass"):
         tot_ms, n, el = 0.0, 0, 0
+        kept = []
         for t in range(warm + steps):
             evs = []
             for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
@@ -292,12 +315,13 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                     f8lin.amax(tensor, st.amax, buf.ws, algo)
                     b.record(stream)
                     evs.append((a, b, tensor.numel()))
-            torch.cuda.synchronize()
             if t >= warm:
-                for a, b, units in evs:
-                    tot_ms += a.elapsed_time(b)
-                    n += 1
-                    el += units
+                kept.extend(evs)
+        torch.cuda.synchronize()
+        for a, b, units in kept:
+            tot_ms += a.elapsed_time(b)
+            n += 1
+            el += units
         k["amax_" + algo] = {"avg_us": round(tot_ms / n * 1e3, 3), "launches": n,
                              "gbs": round(2 * el / (tot_ms * 1e-3) / 1e9, 1),
                              "frac_hbm_peak": round(2 * el / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

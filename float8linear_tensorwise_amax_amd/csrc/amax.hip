@@ -6,7 +6,9 @@
 //            workgroup to finish (ticket counter) publishes the result and
 //            clears the slot and ticket for the next call.
 //   twopass: the same per-workgroup reduction writes one partial per
-//            workgroup; a second launch of one workgroup reduces them.
+//            workgroup; the second pass reduces them -- inside the prologue of
+//            the cast kernel that consumes the amax (f8lin_forward /
+//            f8lin_backward), or as a one-workgroup launch (f8lin_amax).
 // Both compute max |x| exactly as the max of the 15-bit magnitude fields, so
 // both give the same bits as a plain max over |x| in any order.  One launch
 // may reduce two tensors (the forward's X and W) with separate workgroups,

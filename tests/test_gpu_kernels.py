@@ -248,10 +248,12 @@ def test_gemm_integer_exact_is_bit_exact(f8):
 @pytest.mark.parametrize("shapes", [((4096, 4096, 4096), (4096, 4096, 4096)),   # the backward pair, big tiles
                                     ((144, 272, 400), (64, 80, 16)),            # small tiles, ragged
                                     ((16, 4096, 4096), (4096, 4096, 16)),       # skinny dgrad + K=16 wgrad
-                                    ((0, 48, 64), (1600, 4800, 1600))])         # an empty entry
+                                    ((0, 48, 64), (1600, 4800, 1600)),          # an empty entry
+                                    ((512, 1024, 4096), (512, 256, 4096), (256, 512, 1024), (48, 96, 160))])
 def test_gemm_batch_equals_single_launches(f8, shapes):
-    """One launch of two GEMMs gives, bit for bit, what two f8lin_gemm calls
-    give; the second is also checked against the oracle on sampled rows."""
+    """One launch of up to four GEMMs gives, bit for bit, what separate
+    f8lin_gemm calls give; the second is also checked against the oracle on
+    sampled rows."""
     print(f"gemm_batch {shapes}", flush=True)
     rng = np.random.default_rng(sum(sum(s) for s in shapes))
     items, singles = [], []
