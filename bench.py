@@ -355,9 +355,30 @@ def cpu_baseline(args, wl, sets, np, torch):
             secs += time.perf_counter() - t0
             flops += 6 * ms * l.N * l.K
         reps += 1
+    # one more sample, op by op (same oracle functions linear_step calls)
+    ops = {"amax": 0.0, "scale": 0.0, "cast_transpose": 0.0, "gemm_refs": 0.0}
+    for l, ms, xb, wb, dyb in host:
+        q = {}
+        for name, t_bits, fmt in (("x", xb, oracle.E4M3), ("w", wb, oracle.E4M3), ("dy", dyb, oracle.E5M2)):
+            t0 = time.perf_counter()
+            a = oracle.amax(t_bits)
+            t1 = time.perf_counter()
+            sc, _ = oracle.scale(a, fmt)
+            t2 = time.perf_counter()
+            q[name] = (oracle.cast(t_bits, fmt, sc)[0], sc)
+            t3 = time.perf_counter()
+            ops["amax"] += t1 - t0
+            ops["scale"] += t2 - t1
+            ops["cast_transpose"] += t3 - t2
+        t0 = time.perf_counter()
+        oracle.forward_ref(q["x"][0], q["w"][0], q["x"][1], q["w"][1])
+        oracle.dgrad_ref(q["dy"][0], q["w"][0], q["dy"][1], q["w"][1])
+        oracle.wgrad_ref(q["dy"][0], q["x"][0], q["dy"][1], q["x"][1])
+        ops["gemm_refs"] += time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": round(secs, 2),
+            "seconds_by_op_one_sample": {k: round(v, 4) for k, v in ops.items()},
             "sample": f"{reps} repetition(s) of one step of {wl.name} on the first {rows_used} rows of X and dY "
                       "per linear (full W): amax, scale, cast+transpose of X, W, dY and the three fp64 GEMM "
                       "references",
