@@ -152,6 +152,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     const int t = start[pi] + off;
     const Problem P = batch.p[pi];
     const int M = P.M, N = P.N, K = P.K;
+    // The inverse scales through the scalar cache (the kernel never writes
+    // them), read here so that the epilogue does not wait for them.
+    typedef const __attribute__((address_space(4))) float cfloat;
+    const float inv_a = *(cfloat *)P.inv_a, inv_b = *(cfloat *)P.inv_b;
     int tm, tn;
     tile_coords<G>(t, P.tiles_m, P.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     // in bit 2 (which swaps the 64-byte halves of the row), so each write is
     // free of bank conflicts.
     __syncthreads();  // every wave is done with the stage buffers
-    const float alpha = P.inv_a[0] * P.inv_b[0];
+    const float alpha = inv_a * inv_b;
     uint8_t *wreg = smem + wave * (WTM * RB);
     const bool odd = lane & 1;
     // bias of this lane's column pair (cpair, cpair + 1) of each 32-column tile j
@@ -335,20 +339,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
+    // All of the wave's staged chunks are read first, then stored with
+    // buffer stores: rows past M lie outside the tile's buffer range and
+    // columns past N get an offset outside it, so no store needs a branch.
     constexpr int CPR = RB / 16;  // 16-byte chunks per row
+    constexpr int NCH = WTM * CPR / 64;
+    const int rows_c = min(BM, M - m0);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.c + (int64_t)m0 * N), (short)0, (int)((uint32_t)rows_c * (uint32_t)N * 2u), 0x00020000);
+    u32x4 vals[NCH];
+    int offs[NCH];
 #pragma unroll
-    for (int k = 0; k < WTM * CPR / 64; ++k) {
+    for (int k = 0; k < NCH; ++k) {
       const int idx = k * 64 + lane;
       const int row = idx / CPR, ch = idx % CPR;
-      const u32x4 v = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ (((row >> 2) & 1) << 6)));
-      const int grow = m0 + wm + row, gcol = n0 + wn + ch * 8;
-      if (grow < M && gcol < N) {
-        u32x4 *dst = (u32x4 *)(P.c + (int64_t)grow * N + gcol);
-        if (batch.nt_stores)
-          __builtin_nontemporal_store(v, dst);
-        else
-          *dst = v;
-      }
+      vals[k] = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ (((row >> 2) & 1) << 6)));
+      const int gcol = n0 + wn + ch * 8;
+      offs[k] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
+    }
+    if (batch.nt_stores) {
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 2);  // nt
+    } else {
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 0);
     }
     __syncthreads();  // staging reads done before the next tile's copies land
   }

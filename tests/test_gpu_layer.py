@@ -71,7 +71,8 @@ def _check_linear(buf, lin, x, w, dy, seed):
 
 @pytest.mark.parametrize("name,algo", [("linear4096_m16", "atomic"), ("linear4096_m16", "twopass"),
                                        ("linear4096_m256", "atomic"), ("linear4096_m4096", "atomic"),
-                                       ("linear4096_m4096", "twopass"), ("linear4096_m65536_outliers", "atomic")])
+                                       ("linear4096_m4096", "twopass"), ("linear4096_m65536_outliers", "atomic"),
+                                       ("linear4096_m65536_outliers", "twopass")])
 def test_single_linear_workloads(f8, name, algo):
     wl = inputs.WORKLOADS[name]
     for lin, x, w, dy in inputs.workload_inputs(wl):
@@ -85,11 +86,12 @@ def test_single_linear_workloads(f8, name, algo):
         torch.cuda.empty_cache()
 
 
-def test_llama3_8b_layer(f8):
+@pytest.mark.parametrize("algo", ["atomic", "twopass"])
+def test_llama3_8b_layer(f8, algo):
     wl = inputs.WORKLOADS["llama3_8b_layer_t8192"]
     for i, (lin, x, w, dy) in enumerate(inputs.workload_inputs(wl)):
-        print(f"llama layer {lin}", flush=True)
-        buf = _run_dynamic(f8, lin, x, w, dy, "atomic")
+        print(f"llama layer {lin} algo={algo}", flush=True)
+        buf = _run_dynamic(f8, lin, x, w, dy, algo)
         _check_linear(buf, lin, x, w, dy, seed=100 + i)
         del buf
         torch.cuda.empty_cache()

@@ -38,7 +38,7 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("algo", ["atomic", "twopass"])
-@pytest.mark.parametrize("shape", [(512, 256, (256, 64, 64)), (8192, 4096, (4096, 1024, 1024)),
+@pytest.mark.parametrize("shape", [(512, 256, (256, 64, 64)), (8192, 4096, (4096, 1024, 1024)), (8192, 4096, (14336, 14336)),
                                    (16, 4096, (4096, 4096)), (300 // 16 * 16, 160, (96, 48, 32, 16))])
 def test_shared_x_equals_separate_forwards(f8, shape, algo):
     M, K, Ns = shape
