@@ -113,6 +113,10 @@ def _ptr(t: Optional[torch.Tensor], dtype=None) -> Optional[int]:
     return t.data_ptr()
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def workspace_bytes() -> int:
     return int(_lib.f8lin_workspace_bytes())
 
@@ -179,7 +183,7 @@ class ScaleView:
 
 def amax(x: torch.Tensor, out: torch.Tensor, ws: torch.Tensor, algo="atomic", stream=None):
     _check(_lib.f8lin_amax(_ptr(x, torch.bfloat16), x.numel(), _ALGO[algo], _ptr(out, torch.float32),
-                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                           _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def cast_transpose(x: torch.Tensor, fmt, mode, state: ScalingState, q: torch.Tensor,
@@ -233,7 +237,7 @@ def _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias,
     return FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
                    _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
                    sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
-                   ws.numel() * ws.element_size(), None if bias is None else _ptr(bias, torch.bfloat16),
+                   _nbytes(ws), None if bias is None else _ptr(bias, torch.bfloat16),
                    1 if w_cast_valid else 0)
 
 
@@ -267,7 +271,7 @@ def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState
     a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr(x8t, torch.uint8), _ptr(w8t, torch.uint8),
                 _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr(dy8t, torch.uint8),
                 sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], _ptr(ws),
-                ws.numel() * ws.element_size(), None if dbias is None else _ptr(dbias, torch.bfloat16),
+                _nbytes(ws), None if dbias is None else _ptr(dbias, torch.bfloat16),
                 None if dbias_ws is None else _ptr(dbias_ws, torch.float32),
                 0 if dbias_ws is None else dbias_ws.numel() * 4)
     _check(_lib.f8lin_backward(ctypes.byref(a), _stream(stream)))

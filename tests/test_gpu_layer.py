@@ -244,3 +244,31 @@ def test_rejected_call_writes_nothing(f8):
         f8.forward(x, w, buf.y, buf.x8, buf.x8t, buf.x8, buf.w8t, buf.sx, buf.sw, buf.ws)
     torch.cuda.synchronize()
     assert torch.all(buf.y == 3.0).item()
+
+
+@pytest.mark.parametrize("mnk", [(16, 16, 16), (144, 160, 96), (288, 272, 400), (1040, 1024, 784)])
+def test_delayed_amax_fold_with_and_without_workspace(f8, mnk):
+    """Delayed scaling folds each tensor's amax into its state during the
+    cast (one atomic max per 128x128 tile).  Through forward and backward,
+    with a workspace and without one (delayed-only calls need none), the
+    folded amax is max |x| bit for bit for 1 to 72 tiles, the workspace is
+    left untouched, and repeating the call is as exact as the first."""
+    M, N, K = mnk
+    x, w, dy = (inputs.random_bf16(s, seed=sd).to(DEV) for s, sd in (((M, K), 1), ((N, K), 2), ((M, N), 3)))
+    want = {nm: np_f32_bits(oracle.amax(bits(t.cpu()))) for nm, t in (("x", x), ("w", w), ("dy", dy))}
+    ws = f8.new_workspace(DEV)
+    for use_ws in (True, False, True):
+        print(f"delayed fold M={M} N={N} K={K} workspace={use_ws}", flush=True)
+        buf = f8.LinearBuffers(M, N, K, DEV)
+        for st in buf.states():  # a history, so that the casts run in delayed mode
+            st.history.fill_(3.0)
+            st.hist_meta[0] = 1
+        wsa = ws if use_ws else None
+        f8.forward(x, w, buf.y, buf.x8, buf.x8t, buf.w8, buf.w8t, buf.sx, buf.sw, wsa, "delayed", "delayed", "atomic")
+        f8.backward(dy, buf.x8t, buf.w8t, buf.dx, buf.dw, buf.dy8, buf.dy8t, buf.sx, buf.sw, buf.sdy, wsa, "delayed",
+                    "atomic")
+        torch.cuda.synchronize()
+        for nm, st in (("x", buf.sx), ("w", buf.sw), ("dy", buf.sdy)):
+            assert f32_bits(st.amax)[0] == want[nm], (nm, use_ws)
+        assert int(torch.count_nonzero(ws)) == 0  # delayed-only calls leave the workspace all zero
+        del buf
