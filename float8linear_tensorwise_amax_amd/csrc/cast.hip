@@ -24,8 +24,11 @@
 //   LDS    : 128 rows x 128 bytes, 16-byte chunks XOR-swizzled by
 //            (row / 16) % 8, which makes both the 128-bit row writes and the
 //            4-byte column reads spread over all banks.
-// Delayed mode also folds max |x| of the tile into state.amax (atomic max on
-// the fp32 bit pattern, which orders like the value for non-negative floats).
+// Delayed mode also folds max |x| into state.amax (atomic max on the fp32
+// bit pattern, which orders like the value for non-negative floats).  Same-
+// address atomics serialise (one per tile cost 6-16 us per cast at 1248-5450
+// tiles, measured), so a delayed-mode workgroup takes four tiles -- four
+// independent 256-thread quarters, each as above -- and issues one atomic.
 //
 // HBM-bound: 2 bytes read + 2 bytes written per element (4 B/elem).
 #include "device_common.h"
@@ -73,18 +76,22 @@ struct CastJob {
   uint8_t *q, *qt;
   float *colsum;          // per-tile column sums (bias gradient), or null
   int tiles_x;
-  int first;
+  int first;              // first workgroup of this tensor
+  int ntiles;
 };
 struct CastJobs {
   CastJob j[2];
   int count;
 };
 
-template <int FMT, int MODE, bool WRITE_T>
-__global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs jobs) {
-  __shared__ uint32_t tile[kTile * kTile / 4];
-  __shared__ uint32_t red[kThreads / 64];
-  __shared__ float colred[kThreads / 64][kTile];
+// TPW tiles per workgroup: thread quarter `sub` (256 threads) casts tile
+// first_tile + sub; a quarter past the tensor's last tile loads and stores
+// nothing.
+template <int FMT, int MODE, bool WRITE_T, int TPW>
+__global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const CastJobs jobs) {
+  __shared__ uint32_t tiles_lds[TPW][kTile * kTile / 4];
+  __shared__ uint32_t red[kThreads * TPW / 64];
+  __shared__ float colred[TPW][kThreads / 64][kTile];
   constexpr float fm = fmt_max<FMT>();
   const int job = (jobs.count > 1 && (int)blockIdx.x >= jobs.j[1].first) ? 1 : 0;
   const CastJob &jb = jobs.j[job];
@@ -92,15 +99,18 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
   const int64_t rows = jb.rows, cols = jb.cols;
   uint8_t *__restrict__ q = jb.q;
   uint8_t *__restrict__ qt = jb.qt;
-  const int local = (int)blockIdx.x - jb.first;
+  const int sub = TPW > 1 ? (int)(threadIdx.x / kThreads) : 0;
+  const int local = ((int)blockIdx.x - jb.first) * TPW + sub;  // this quarter's tile
+  const bool live = TPW == 1 || local < jb.ntiles;
+  uint32_t *tile = tiles_lds[sub];
 
-  const int t = threadIdx.x;
+  const int t = threadIdx.x % kThreads;
   const int64_t row0 = (int64_t)(local / jb.tiles_x) * kTile;
   const int64_t col0 = (int64_t)(local % jb.tiles_x) * kTile;
   const int c16 = t & 7;
   const int rsub = t >> 3;
   const int64_t gcol = col0 + c16 * 16;
-  const bool col_ok = gcol < cols;
+  const bool col_ok = live && gcol < cols;
 
   u32x4 in[4][2];
 #pragma unroll
@@ -193,16 +203,16 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
     // Out-of-range elements were loaded as +0 and cannot raise the max.
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
-    if ((t & 63) == 0) red[t >> 6] = mag;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mag;
   }
 
   if constexpr (WRITE_T || MODE == F8LIN_DELAYED) __syncthreads();
 
   if constexpr (MODE == F8LIN_DELAYED) {
-    if (t == 0) {
+    if (threadIdx.x == 0) {  // one atomic for the workgroup's TPW tiles
       uint32_t m = red[0];
 #pragma unroll
-      for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+      for (int w = 1; w < kThreads * TPW / 64; ++w) m = max(m, red[w]);
       atomicMax(reinterpret_cast<uint32_t *>(jb.amax_acc), m << 16);
     }
   }
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
       out[2][m] = e2;
       out[3][m] = e3;
     }
-    if (qrow < cols && qcol < rows) {
+    if (live && qrow < cols && qcol < rows) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4 *>(qt + (qrow + b) * rows + qcol) = out[b];
     }
@@ -242,11 +252,11 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(const CastJobs
     const int lane = t & 63, wave = t >> 6;
     if (lane < 8) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) colred[wave][lane * 16 + e] = cs[e];
+      for (int e = 0; e < 16; ++e) colred[sub][wave][lane * 16 + e] = cs[e];
     }
     __syncthreads();
-    if (t < kTile && col0 + t < cols) {
-      const float v = ((colred[0][t] + colred[1][t]) + colred[2][t]) + colred[3][t];
+    if (live && t < kTile && col0 + t < cols) {
+      const float v = ((colred[sub][0][t] + colred[sub][1][t]) + colred[sub][2][t]) + colred[sub][3][t];
       jb.colsum[(row0 / kTile) * cols + col0 + t] = v;
     }
   }
@@ -298,12 +308,18 @@ __global__ __launch_bounds__(kDbCols * kDbGroups) void dbias_kernel(const float 
   }
 }
 
+// Tiles per workgroup: four in delayed mode (one atomic per four tiles),
+// one in dynamic mode.
+template <int MODE>
+constexpr int tiles_per_wg() { return MODE == F8LIN_DELAYED ? 4 : 1; }
+
 template <int FMT, int MODE>
 void launch_ct(unsigned grid, const CastJobs &jobs, bool write_t, hipStream_t stream) {
+  constexpr int TPW = tiles_per_wg<MODE>();
   if (write_t)
-    cast_transpose_kernel<FMT, MODE, true><<<grid, kThreads, 0, stream>>>(jobs);
+    cast_transpose_kernel<FMT, MODE, true, TPW><<<grid, kThreads * TPW, 0, stream>>>(jobs);
   else
-    cast_transpose_kernel<FMT, MODE, false><<<grid, kThreads, 0, stream>>>(jobs);
+    cast_transpose_kernel<FMT, MODE, false, TPW><<<grid, kThreads * TPW, 0, stream>>>(jobs);
 }
 
 }  // namespace
@@ -315,15 +331,16 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
   // of a launch or for none.
   CastJobs jobs = {};
   jobs.count = count;
-  int64_t total = 0;
+  const int64_t tpw = mode == F8LIN_DELAYED ? tiles_per_wg<F8LIN_DELAYED>() : tiles_per_wg<F8LIN_DYNAMIC>();
+  int64_t total = 0;  // workgroups
   for (int i = 0; i < count; ++i) {
     const CastTensor &t = ts[i];
     const int64_t gx = t.cols > 0 ? (t.cols + kTile - 1) / kTile : 1;
     const int64_t gy = t.rows > 0 ? (t.rows + kTile - 1) / kTile : 1;
     jobs.j[i] = CastJob{t.x,          t.rows,       t.cols,      t.st->amax, t.partials, t.npartials,
                         t.st->history, t.st->amax, t.st->scale, t.q,        t.qt,       t.colsum,
-                        (int)gx,       (int)total};
-    total += gx * gy;
+                        (int)gx,       (int)total,  (int)(gx * gy)};
+    total += (gx * gy + tpw - 1) / tpw;
   }
   // (An empty tensor may pass a null qt; its workgroup writes no rows.)
   bool write_t = false;
