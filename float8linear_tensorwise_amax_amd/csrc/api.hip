@@ -259,6 +259,12 @@ size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N) {
   return (size_t)dbias_tiles(M) * (size_t)N * sizeof(float);
 }
 
+size_t f8lin_backward_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return 0;
+  // dgrad: (M, K) contracted over N; wgrad: (N, K) contracted over M
+  return split_workspace_bytes(M, K, N) + split_workspace_bytes(N, K, M);
+}
+
 const char *f8lin_status_str(int status) {
   switch (status) {
     case F8LIN_OK: return "F8LIN_OK";
@@ -350,25 +356,31 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
       missing(a.dw, a.N * a.K))
     return F8LIN_EINVAL;
   if (!aligned16(a.dy) || !aligned16(a.x8t) || !aligned16(a.w8t) || !aligned16(a.dx) || !aligned16(a.dw) ||
-      !aligned16(a.dy8) || !aligned16(a.dy8t) || !aligned16(a.dbias) || !aligned16(a.dbias_ws))
+      !aligned16(a.dy8) || !aligned16(a.dy8t) || !aligned16(a.dbias) || !aligned16(a.dbias_ws) ||
+      !aligned16(a.gemm_ws))
     return F8LIN_EALIGN;
+  // the part of gemm_ws that split GEMMs may write
+  const int64_t gemm_ws = a.gemm_ws ? (int64_t)std::min<size_t>(a.gemm_ws_bytes,
+                                                                 f8lin_backward_gemm_workspace_bytes(a.M, a.N, a.K))
+                                    : 0;
   const bool need_ws = a.mode_dy == F8LIN_DYNAMIC;
   if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
   const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
   if (db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
   const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
-  const Range outs[9] = {{a.dx, 2 * mk},
-                         {a.dw, 2 * nk},
-                         {a.dy8, mn},
-                         {a.dy8t, mn},
-                         {a.sdy.scale, 8},
-                         {a.sdy.amax, 4},
-                         {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0},
-                         {a.dbias, a.dbias ? 2 * a.N : 0},
-                         {a.dbias_ws, db_ws}};
+  const Range outs[10] = {{a.dx, 2 * mk},
+                          {a.dw, 2 * nk},
+                          {a.dy8, mn},
+                          {a.dy8t, mn},
+                          {a.sdy.scale, 8},
+                          {a.sdy.amax, 4},
+                          {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0},
+                          {a.dbias, a.dbias ? 2 * a.N : 0},
+                          {a.dbias_ws, db_ws},
+                          {a.gemm_ws, gemm_ws}};
   const Range ins[6] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
                         {a.sx.scale, 8}, {a.sw.scale, 8}, {a.sdy.history, a.mode_dy == F8LIN_DELAYED ? 64 : 0}};
-  if (any_overlap(outs, 9, ins, 6)) return F8LIN_EINVAL;
+  if (any_overlap(outs, 10, ins, 6)) return F8LIN_EINVAL;
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a.ws;
@@ -388,7 +400,7 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
   //   dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
   const GemmDesc g[2] = {{a.dy8, a.w8t, a.sdy.scale + 1, a.sw.scale + 1, a.dx, a.M, a.K, a.N},
                          {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
-  return status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s));
+  return status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws));
 }
 
 int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream) {

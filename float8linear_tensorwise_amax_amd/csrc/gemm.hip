@@ -67,6 +67,7 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
 constexpr int kXcds = 8;
@@ -78,10 +79,11 @@ constexpr int kOutOfRange = (int)0x80000000u;
 struct Problem {
   const uint8_t *a, *b;
   const float *inv_a, *inv_b;
-  uint16_t *c;
+  uint16_t *c;           // (M, N) bf16; split problems: splits x (M, N) fp32 partial sums
   const uint16_t *bias;  // (N) bf16 or null
   int M, N, K;
   int tiles_m, tiles_n;
+  int splits;  // split problems: K-block ranges, each a partial product of its own
 };
 struct Batch {
   Problem p[kMaxGemms];
@@ -105,7 +107,11 @@ __device__ __forceinline__ void tile_coords(int local, int tiles_m, int tiles_n,
 template <bool B>
 using bool_t = std::integral_constant<bool, B>;
 
-template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G>
+// PARTIAL: every problem is split along K into P.splits ranges of whole K
+// blocks; the tile list holds every (range, tile) pair, and a tile writes its
+// range's fp32 partial product, unscaled, to slab `range` of P.c (summed,
+// scaled and rounded by split_reduce_kernel).
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool PARTIAL>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const Batch batch) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   int start[kMaxGemms], len[kMaxGemms], total = 0;
 #pragma unroll
   for (int i = 0; i < kMaxGemms; ++i) {
-    const int T = i < batch.count ? batch.p[i].tiles_m * batch.p[i].tiles_n : 0;
+    const int T = i < batch.count ? batch.p[i].tiles_m * batch.p[i].tiles_n * (PARTIAL ? batch.p[i].splits : 1) : 0;
     const int per = T / kXcds, rem = T % kXcds;
     start[i] = xcd * per + min(xcd, rem);
     len[i] = per + (xcd < rem ? 1 : 0);
@@ -149,9 +155,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         off -= len[i];
         pi = i + 1;
       }
-    const int t = start[pi] + off;
+    int t = start[pi] + off;
     const Problem P = batch.p[pi];
-    const int M = P.M, N = P.N, K = P.K;
+    const int M = P.M, N = P.N;
+    const int ld = P.K;  // row stride of both operands
+    // the K range this tile contracts: all of K, or its split's whole K blocks
+    int K = P.K, kbase = 0, range = 0;
+    if constexpr (PARTIAL) {
+      const int per = P.tiles_m * P.tiles_n;
+      range = t / per;
+      t -= range * per;
+      const int nkb = (P.K + kBK - 1) / kBK;
+      const int kb0 = range * nkb / P.splits, kb1 = (range + 1) * nkb / P.splits;
+      kbase = kb0 * kBK;
+      K = min(kb1 * kBK, P.K) - kbase;
+    }
     // The inverse scales through the scalar cache (the kernel never writes
     // them), read here so that the epilogue does not wait for them.
     typedef const __attribute__((address_space(4))) float cfloat;
@@ -160,10 +178,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     tile_coords<G>(t, P.tiles_m, P.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
-    const __amdgpu_buffer_rsrc_t rsa =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(P.a + (int64_t)m0 * K), (short)0, rows_a * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsb =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(P.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+    // (rows past the tile's last row lie outside the range; bytes past the
+    // range's K are masked in issue_one)
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.a + (int64_t)m0 * ld + kbase), (short)0, rows_a * ld - kbase, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.b + (int64_t)n0 * ld + kbase), (short)0, rows_b * ld - kbase, 0x00020000);
 
     // Global offset (without the K block base) and K byte of each 16-byte
     // slot this lane copies: A slot s = (wave * LA + j) * 64 + lane, same for B.
@@ -172,14 +192,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     for (int j = 0; j < LA; ++j) {
       const int s = (wave * LA + j) * 64 + lane;
       const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-      offa[j] = r * K + c * 16;
+      offa[j] = r * ld + c * 16;
       kca[j] = c * 16;
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
       const int s = (wave * LB + j) * 64 + lane;
       const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-      offb[j] = r * K + c * 16;
+      offb[j] = r * ld + c * 16;
       kcb[j] = c * 16;
     }
     // copy q (0 .. LQ-1) of K block kt into stage kt & 1
@@ -297,6 +317,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (; s + 2 < nk; ++s) block(s, bool_t<true>(), bool_t<true>());
       if (s + 1 < nk) block(s++, bool_t<true>(), bool_t<false>());
       block(s, bool_t<false>(), bool_t<false>());
+    }
+
+    if constexpr (PARTIAL) {
+      // fp32 partial product, unscaled: lane (column c = lane & 31, half h)
+      // holds rows 8*(v>>2) + 4*h + (v&3) of each 32x32 tile; 32 lanes write
+      // 128 contiguous bytes of a row.  Rows past M lie outside the slab's
+      // range, columns past N get an offset outside it.
+      const int rows_c = min(BM, M - m0);
+      const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(reinterpret_cast<float *>(P.c) + ((int64_t)range * M + m0) * N), (short)0, rows_c * N * 4,
+          0x00020000);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn + j * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rsp, vo, 0, 0);
+          }
+        }
+      __syncthreads();  // every wave is done with the stage buffers before the next tile's copies
+      continue;
     }
 
     // Epilogue.  Lane (column c = lane & 31, half h = lane >> 5) holds, per
@@ -451,44 +496,118 @@ void launch_skinny(const Problem &p, hipStream_t stream) {
   }
 }
 
-template <int FA, int FB>
-void launch_fmt(Batch &b, hipStream_t stream) {
-  // skinny problems get their own launches; the rest share one
-  Batch rest{};
-  for (int i = 0; i < b.count; ++i) {
-    if (b.p[i].M <= kSkinnyMaxM)
-      launch_skinny<FA, FB>(b.p[i], stream);
-    else
-      rest.p[rest.count++] = b.p[i];
+// C = bf16(alpha * (sum over ranges of the fp32 partials, in range order)),
+// the same fp32 scaling and rounding as the tiled kernel's epilogue; four
+// elements per thread (M * N is a multiple of 16).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ part, int splits, int64_t mn,
+                                                           const float *inv_a, const float *inv_b,
+                                                           uint16_t *__restrict__ c) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  float4 acc = *reinterpret_cast<const float4 *>(part + i);
+  for (int r = 1; r < splits; ++r) {
+    const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)r * mn + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
-  b = rest;
-  if (b.count == 0) return;
-  int64_t big = 0;
-  for (int i = 0; i < b.count; ++i) big += (int64_t)((b.p[i].M + 255) / 256) * ((b.p[i].N + 255) / 256);
-  const bool use_big = big >= kCUs;
-  const int bm = use_big ? 256 : 128;
-  int tiles = 0;
+  const float alpha = inv_a[0] * inv_b[0];
+  const bf16x2 lo = __builtin_convertvector(f32x2{acc.x * alpha, acc.y * alpha}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector(f32x2{acc.z * alpha, acc.w * alpha}, bf16x2);
+  *reinterpret_cast<u32x2 *>(c + i) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+template <int FA, int FB>
+void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, hipStream_t stream) {
+  // skinny problems get their own launches; problems with few long tiles are
+  // split along K when there is room for their partials; the rest share one
+  Batch rest{}, split{};
+  const Problem *orig[kMaxGemms];
+  size_t used = 0;
   for (int i = 0; i < b.count; ++i) {
     Problem &p = b.p[i];
-    p.tiles_m = (p.M + bm - 1) / bm;
-    p.tiles_n = (p.N + bm - 1) / bm;
-    tiles += p.tiles_m * p.tiles_n;
+    const int s = p.M <= kSkinnyMaxM ? 1 : split_factor(p.M, p.N, p.K);
+    const size_t need = (size_t)s * p.M * p.N * 4;
+    if (p.M <= kSkinnyMaxM) {
+      launch_skinny<FA, FB>(p, stream);
+    } else if (s > 1 && split_ws && used + need <= split_bytes) {
+      orig[split.count] = &b.p[i];
+      Problem &q = split.p[split.count++];
+      q = p;
+      q.c = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(split_ws) + used);
+      q.splits = s;
+      q.bias = nullptr;
+      used += need;
+    } else {
+      rest.p[rest.count++] = p;
+    }
   }
-  if (tiles == 0) return;
-  // With several waves of tiles per CU the output would only evict operand
-  // lines from the caches: stream it (measured: -3.5% time at 65536 x 4096 x
-  // 4096, +2% at 4096^3 where each CU writes one tile).
-  b.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
-  if (use_big) {
-    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(b);
-  } else {
-    gemm_fp8_tn_kernel<FA, FB, 128, 128, 2, 2, 2, 8><<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(b);
+  if (split.count > 0) {
+    int tiles = 0;
+    for (int i = 0; i < split.count; ++i) {
+      Problem &p = split.p[i];
+      p.tiles_m = (p.M + 255) / 256;
+      p.tiles_n = (p.N + 255) / 256;
+      tiles += p.tiles_m * p.tiles_n * p.splits;
+    }
+    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(split);
+  }
+  if (rest.count > 0) {
+    int64_t big = 0;
+    for (int i = 0; i < rest.count; ++i) big += (int64_t)((rest.p[i].M + 255) / 256) * ((rest.p[i].N + 255) / 256);
+    const bool use_big = big >= kCUs;
+    const int bm = use_big ? 256 : 128;
+    int tiles = 0;
+    for (int i = 0; i < rest.count; ++i) {
+      Problem &p = rest.p[i];
+      p.tiles_m = (p.M + bm - 1) / bm;
+      p.tiles_n = (p.N + bm - 1) / bm;
+      p.splits = 1;
+      tiles += p.tiles_m * p.tiles_n;
+    }
+    // With several waves of tiles per CU the output would only evict operand
+    // lines from the caches: stream it (measured: -3.5% time at 65536 x 4096 x
+    // 4096, +2% at 4096^3 where each CU writes one tile).
+    rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
+    if (use_big) {
+      gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, false>
+          <<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(rest);
+    } else {
+      gemm_fp8_tn_kernel<FA, FB, 128, 128, 2, 2, 2, 8, false>
+          <<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(rest);
+    }
+  }
+  for (int i = 0; i < split.count; ++i) {
+    const Problem &q = split.p[i];
+    const int64_t mn = (int64_t)q.M * q.N;
+    split_reduce_kernel<<<(unsigned)((mn / 4 + 255) / 256), 256, 0, stream>>>(
+        reinterpret_cast<const float *>(q.c), q.splits, mn, q.inv_a, q.inv_b, orig[i]->c);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream) {
+int split_factor(int64_t M, int64_t N, int64_t K) {
+  // Few output tiles with a long contraction leave most CUs idle (e.g. a
+  // weight gradient over many tokens with a small weight): split K into up
+  // to eight ranges of at least eight 128-byte K blocks, so that the
+  // (range, tile) pairs about fill the 256 CUs.
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (M <= kSkinnyMaxM || tiles == 0 || tiles * 2 > kCUs) return 1;
+  const int64_t nkb = (K + kBK - 1) / kBK;
+  int64_t s = std::min<int64_t>(kCUs / tiles, nkb / 8);
+  s = std::min<int64_t>(s, 8);
+  return s > 1 ? (int)s : 1;
+}
+
+size_t split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int s = split_factor(M, N, K);
+  return s > 1 ? (size_t)s * M * N * 4 : 0;
+}
+
+hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream, void *split_ws,
+                        size_t split_bytes) {
   Batch b{};
   for (int i = 0; i < count; ++i) {
     if (d[i].M == 0 || d[i].N == 0) continue;
@@ -502,16 +621,18 @@ hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipS
     p.M = (int)d[i].M;
     p.N = (int)d[i].N;
     p.K = (int)d[i].K;
+    p.splits = 1;
   }
   if (b.count == 0) return hipSuccess;
+  float *ws = reinterpret_cast<float *>(split_ws);
   if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E4M3)
-    launch_fmt<0, 0>(b, stream);
+    launch_fmt<0, 0>(b, ws, split_bytes, stream);
   else if (fmt_a == F8LIN_E5M2 && fmt_b == F8LIN_E4M3)
-    launch_fmt<1, 0>(b, stream);
+    launch_fmt<1, 0>(b, ws, split_bytes, stream);
   else if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E5M2)
-    launch_fmt<0, 1>(b, stream);
+    launch_fmt<0, 1>(b, ws, split_bytes, stream);
   else
-    launch_fmt<1, 1>(b, stream);
+    launch_fmt<1, 1>(b, ws, split_bytes, stream);
   return hipGetLastError();
 }
 

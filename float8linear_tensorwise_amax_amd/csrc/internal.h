@@ -66,7 +66,15 @@ struct GemmDesc {
   int64_t M, N, K;
   const uint16_t *bias = nullptr;  // (N) bf16 added to every row, or null
 };
-hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream);
+// split_ws (optional, 16-byte aligned): room for the fp32 partial products of
+// problems split along K (split_factor > 1); a problem that does not fit
+// runs unsplit.  Contents need no initialisation.
+hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream,
+                        void *split_ws = nullptr, size_t split_bytes = 0);
+// K ranges a problem is split into when a partial-product workspace is given
+// (1: not split), and the bytes its partials need.
+int split_factor(int64_t M, int64_t N, int64_t K);
+size_t split_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_delayed_update(const f8lin_state *states, int n, hipStream_t stream);
 

@@ -61,13 +61,16 @@ class BwdArgs(ctypes.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("dy", _vp), ("x8t", _vp), ("w8t", _vp),
                 ("dx", _vp), ("dw", _vp), ("dy8", _vp), ("dy8t", _vp), ("sx", State), ("sw", State),
                 ("sdy", State), ("mode_dy", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
-                ("dbias", _vp), ("dbias_ws", _vp), ("dbias_ws_bytes", ctypes.c_size_t)]
+                ("dbias", _vp), ("dbias_ws", _vp), ("dbias_ws_bytes", ctypes.c_size_t), ("gemm_ws", _vp),
+                ("gemm_ws_bytes", ctypes.c_size_t)]
 
 
 _lib.f8lin_workspace_bytes.argtypes = []
 _lib.f8lin_workspace_bytes.restype = ctypes.c_size_t
 _lib.f8lin_dbias_workspace_bytes.argtypes = [_i64, _i64]
 _lib.f8lin_dbias_workspace_bytes.restype = ctypes.c_size_t
+_lib.f8lin_backward_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.f8lin_backward_gemm_workspace_bytes.restype = ctypes.c_size_t
 _lib.f8lin_status_str.argtypes = [_int]
 _lib.f8lin_status_str.restype = ctypes.c_char_p
 _lib.f8lin_amax.argtypes = [_vp, _i64, _int, _vp, _vp, ctypes.c_size_t, _vp]
@@ -123,6 +126,16 @@ def workspace_bytes() -> int:
 
 def dbias_workspace_bytes(M: int, N: int) -> int:
     return int(_lib.f8lin_dbias_workspace_bytes(M, N))
+
+
+def backward_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.f8lin_backward_gemm_workspace_bytes(M, N, K))
+
+
+def new_backward_gemm_workspace(M: int, N: int, K: int, device="cuda") -> Optional[torch.Tensor]:
+    """Scratch for split backward GEMMs (uninitialised), or None when no GEMM of this shape splits."""
+    n = backward_gemm_workspace_bytes(M, N, K)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def new_dbias_workspace(M: int, N: int, device="cuda") -> torch.Tensor:
@@ -261,7 +274,9 @@ def forward_shared_x(x, x8, x8t, sx: ScalingState, ws, linears, mode_x="dynamic"
 
 
 def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState, sdy: ScalingState, ws,
-             mode_dy="dynamic", algo="atomic", stream=None, dbias=None, dbias_ws=None):
+             mode_dy="dynamic", algo="atomic", stream=None, dbias=None, dbias_ws=None, gemm_ws=None):
+    """gemm_ws: optional scratch (backward_gemm_workspace_bytes(M, N, K) bytes) with which GEMMs that have
+    few output tiles and a long contraction run split along K."""
     M, N = dy.shape
     K = x8t.shape[0]
     if tuple(dx.shape) != (M, K) or tuple(dw.shape) != (N, K) or tuple(w8t.shape) != (K, N):
@@ -273,7 +288,7 @@ def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState
                 sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], _ptr(ws),
                 _nbytes(ws), None if dbias is None else _ptr(dbias, torch.bfloat16),
                 None if dbias_ws is None else _ptr(dbias_ws, torch.float32),
-                0 if dbias_ws is None else dbias_ws.numel() * 4)
+                0 if dbias_ws is None else dbias_ws.numel() * 4, _ptr(gemm_ws), _nbytes(gemm_ws))
     _check(_lib.f8lin_backward(ctypes.byref(a), _stream(stream)))
 
 
@@ -307,6 +322,7 @@ class LinearBuffers:
         self.ws = new_workspace(device)
         self.dbias = torch.empty((N,), **bf) if with_bias else None
         self.dbias_ws = new_dbias_workspace(M, N, device) if with_bias else None
+        self.gemm_ws = new_backward_gemm_workspace(M, N, K, device)
 
     def forward(self, x, w, mode="dynamic", algo="atomic", stream=None, bias=None):
         forward(x, w, self.y, self.x8, self.x8t, self.w8, self.w8t, self.sx, self.sw, self.ws, mode, mode, algo,
@@ -315,7 +331,7 @@ class LinearBuffers:
 
     def backward(self, dy, mode="dynamic", algo="atomic", stream=None):
         backward(dy, self.x8t, self.w8t, self.dx, self.dw, self.dy8, self.dy8t, self.sx, self.sw, self.sdy,
-                 self.ws, mode, algo, stream, self.dbias, self.dbias_ws)
+                 self.ws, mode, algo, stream, self.dbias, self.dbias_ws, self.gemm_ws)
         return self.dx, self.dw
 
     def states(self):

@@ -109,8 +109,11 @@ class _Float8LinearFn(torch.autograd.Function):
         if ctx.b_dtype is not None:
             db = torch.empty((N,), dtype=torch.bfloat16, device=dev)
             db_ws = f8lin.new_dbias_workspace(M, N, dev)
+        # scratch for GEMMs split along their contraction (None when none splits at this shape)
+        gemm_ws = f8lin.new_backward_gemm_workspace(M, N, K, dev)
         f8lin.backward(dy, x8t, w8t, dx, dw, dy8, dy8t, f8lin.ScaleView(sx_scale), f8lin.ScaleView(sw_scale),
-                       layer.sdy, layer.ws, layer._mode("dy"), layer.config.amax_algo, dbias=db, dbias_ws=db_ws)
+                       layer.sdy, layer.ws, layer._mode("dy"), layer.config.amax_algo, dbias=db, dbias_ws=db_ws,
+                       gemm_ws=gemm_ws)
         return dx[:ctx.M0], dw.to(ctx.w_dtype), (None if db is None else db.to(ctx.b_dtype)), None
 
 

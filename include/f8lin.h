@@ -191,7 +191,16 @@ typedef struct {
  * bits on every run -- and rounded once to bf16); NULL for none.  It needs
  * dbias_ws, a scratch buffer of >= f8lin_dbias_workspace_bytes(M, N) bytes
  * for the per-tile column sums (contents need no initialisation).  Both
- * 16-byte aligned. */
+ * 16-byte aligned.
+ * gemm_ws: optional (NULL = none) scratch for GEMMs split along their
+ * contraction: a GEMM with few 256x256 output tiles and a long contraction
+ * (typically dW of a small weight over many tokens) leaves most CUs idle, so
+ * with room in gemm_ws (f8lin_backward_gemm_workspace_bytes(M, N, K) bytes;
+ * contents need no initialisation; 16-byte aligned) it runs as up to eight
+ * K ranges whose fp32 partial products a second kernel sums in range order
+ * (the same bits on every run), scales and rounds to bf16.  The summation
+ * order differs from the unsplit GEMM's, so the results may differ from it
+ * in the last bits, within the GEMM tolerance. */
 typedef struct {
   int64_t M, N, K;
   const uint16_t *dy;           /* input (M, N) */
@@ -206,11 +215,19 @@ typedef struct {
   uint16_t *dbias;              /* (N) bf16 output, or NULL */
   float *dbias_ws;              /* scratch for dbias, or NULL */
   size_t dbias_ws_bytes;
+  void *gemm_ws;                /* scratch for split GEMMs, or NULL */
+  size_t gemm_ws_bytes;
 } f8lin_bwd_args;
 
 /* Bytes of dbias_ws that f8lin_backward needs for an (M, N) dY:
  * max(1, ceil(M / 128)) * N * 4. */
 size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N);
+
+/* Bytes of gemm_ws with which f8lin_backward splits every GEMM of an
+ * (M, N, K) layer that it would split (0: none is split at this shape; also
+ * 0 for invalid dimensions).  With less, GEMMs whose partials do not fit run
+ * unsplit. */
+size_t f8lin_backward_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 int f8lin_forward(const f8lin_fwd_args *args, void *stream);
 

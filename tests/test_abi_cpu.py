@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_forward", "f8lin_backward",
                      "f8lin_delayed_update", "f8lin_gemm", "f8lin_gemm_batch", "f8lin_cast_f32", "f8lin_workspace_bytes",
-                     "f8lin_dbias_workspace_bytes",
+                     "f8lin_dbias_workspace_bytes", "f8lin_backward_gemm_workspace_bytes",
                      "f8lin_status_str"):
         assert required in names
 
@@ -166,7 +166,8 @@ class Bwd(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in ("dy", "x8t", "w8t", "dx", "dw", "dy8", "dy8t")] + \
                [("sx", State), ("sw", State), ("sdy", State), ("mode_dy", ctypes.c_int), ("algo", ctypes.c_int),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("dbias", ctypes.c_void_p),
-                ("dbias_ws", ctypes.c_void_p), ("dbias_ws_bytes", ctypes.c_size_t)]
+                ("dbias_ws", ctypes.c_void_p), ("dbias_ws_bytes", ctypes.c_size_t), ("gemm_ws", ctypes.c_void_p),
+                ("gemm_ws_bytes", ctypes.c_size_t)]
 
 
 def test_backward_rejections(lib):
@@ -184,7 +185,7 @@ def test_backward_rejections(lib):
     def args(**kw):
         a = Bwd(288, 48, 64, A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB,
                 State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None),
-                State(AMAX + 128, SCALE + 128, None, None), 0, 0, WS, WSB, None, None, 0)
+                State(AMAX + 128, SCALE + 128, None, None), 0, 0, WS, WSB, None, None, 0, None, 0)
         for k, v in kw.items():
             setattr(a, k, v)
         return a
@@ -197,6 +198,44 @@ def test_backward_rejections(lib):
     assert f(ctypes.byref(args(dbias=DB + 2, dbias_ws=DBWS, dbias_ws_bytes=need)), None) == EALIGN
     assert f(ctypes.byref(args(dbias=DB, dbias_ws=A, dbias_ws_bytes=need)), None) == EINVAL  # scratch is dY
     assert f(ctypes.byref(args(dbias=A + MB, dbias_ws=DBWS, dbias_ws_bytes=need)), None) == EINVAL  # dbias in x8t
+
+
+def test_backward_gemm_workspace(lib):
+    """Split-GEMM scratch: its size query, and a misaligned or overlapping
+    gemm_ws is rejected (every call here fails validation: nothing runs)."""
+    g = lib.f8lin_backward_gemm_workspace_bytes
+    g.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    g.restype = ctypes.c_size_t
+    # dW of a 256 x 256 weight over 4096 tokens: one output tile, 32 K blocks -> four K ranges of fp32 partials
+    assert g(4096, 256, 256) == 4 * 256 * 256 * 4
+    # dX (M, K) of a few rows with a long contraction over N splits too; square layers split nothing
+    assert g(256, 4096, 256) == 4 * 256 * 256 * 4 + 0
+    assert g(4096, 4096, 4096) == 0 and g(16, 4096, 4096) == 0
+    assert g(4096, 4096, 4095) == 0 and g(-16, 16, 16) == 0  # invalid dimensions
+    # the GPT-block output projection (1600 -> 1600 over 12288 tokens): dW splits five ways
+    assert g(12288, 1600, 1600) == 5 * 1600 * 1600 * 4
+
+    f = lib.f8lin_backward
+    f.argtypes = [ctypes.POINTER(Bwd), ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    SL = 16 << 20  # 16 MiB between fake buffers
+    M, N, K = 4096, 256, 256
+    need = g(M, N, K)
+
+    def args(**kw):
+        a = Bwd(M, N, K, A, A + SL, A + 2 * SL, A + 3 * SL, A + 4 * SL, A + 5 * SL, A + 6 * SL,
+                State(AMAX, SCALE, None, None), State(AMAX + 64, SCALE + 64, None, None),
+                State(AMAX + 128, SCALE + 128, None, None), 0, 0, WS, WSB, None, None, 0, None, 0)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    GW = A + 8 * SL
+    assert f(ctypes.byref(args(gemm_ws=GW + 8, gemm_ws_bytes=need)), None) == EALIGN
+    assert f(ctypes.byref(args(gemm_ws=A + 3 * SL, gemm_ws_bytes=need)), None) == EINVAL    # scratch is dX
+    assert f(ctypes.byref(args(gemm_ws=A + SL - 4096, gemm_ws_bytes=need)), None) == EINVAL  # runs into x8t
+    # with too little scratch only what fits would split, but overlap is checked on that part
+    assert f(ctypes.byref(args(gemm_ws=A + 2 * SL, gemm_ws_bytes=64)), None) == EINVAL      # scratch is w8t
 
 
 def test_forward_rejections(lib):

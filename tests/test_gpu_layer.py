@@ -272,3 +272,34 @@ def test_delayed_amax_fold_with_and_without_workspace(f8, mnk):
             assert f32_bits(st.amax)[0] == want[nm], (nm, use_ws)
         assert int(torch.count_nonzero(ws)) == 0  # delayed-only calls leave the workspace all zero
         del buf
+
+
+@pytest.mark.parametrize("mnk", [(4096, 256, 256), (256, 4096, 256), (2000, 272, 144), (12288, 1600, 1600)])
+def test_backward_split_gemms(f8, mnk):
+    """GEMMs with few output tiles and a long contraction run split along K
+    when backward gets a split-GEMM workspace: four ranges for dW of a 256 x
+    256 weight over 4096 tokens, four for dX of 256 rows over N = 4096, two
+    uneven ranges (the last one ragged) for dW over 2000 tokens, five for the
+    GPT block's output projection.  Split and unsplit results both meet the
+    GEMM tolerance against the oracle, and the split ones are the same bits
+    on every run."""
+    M, N, K = mnk
+    assert f8.backward_gemm_workspace_bytes(M, N, K) > 0
+    lin = inputs.Linear("split", M, K, N)
+    x, w, dy = (inputs.random_bf16(s, seed=sd, std=st) for s, sd, st in
+                (((M, K), 7, 1.0), ((N, K), 8, K ** -0.5), ((M, N), 9, 1e-3 ** 0.5)))
+    print(f"split backward M={M} N={N} K={K}", flush=True)
+    buf = _run_dynamic(f8, lin, x, w, dy, "twopass")  # LinearBuffers passes the split workspace
+    assert buf.gemm_ws is not None
+    ref = oracle.linear_step(bits(x), bits(w), bits(dy), gemms=False)
+    _check_gemms(buf, ref, lin, seed=M + N)
+    dx1, dw1 = buf.dx.clone(), buf.dw.clone()
+    buf.backward(dy.to(DEV), "dynamic", "twopass")
+    torch.cuda.synchronize()
+    assert torch.equal(buf.dx.view(torch.int16), dx1.view(torch.int16))
+    assert torch.equal(buf.dw.view(torch.int16), dw1.view(torch.int16))
+    # unsplit (no workspace): also within tolerance
+    buf.gemm_ws = None
+    buf.backward(dy.to(DEV), "dynamic", "twopass")
+    torch.cuda.synchronize()
+    _check_gemms(buf, ref, lin, seed=M + N)
