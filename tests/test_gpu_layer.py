@@ -303,3 +303,24 @@ def test_backward_split_gemms(f8, mnk):
     buf.backward(dy.to(DEV), "dynamic", "twopass")
     torch.cuda.synchronize()
     _check_gemms(buf, ref, lin, seed=M + N)
+
+
+def test_backward_split_workspace_too_small_for_both(f8):
+    """At M = N = 2048, K = 256 both backward GEMMs split two ways.  With
+    scratch for the first (dX) only, dX runs split and dW unsplit; with none,
+    neither does.  All of them meet the GEMM tolerance."""
+    M, N, K = 2048, 2048, 256
+    full = f8.backward_gemm_workspace_bytes(M, N, K)
+    assert full == 2 * (2 * M * K * 4)  # two ranges of fp32 partials for each of dX (M, K) and dW (N, K)
+    lin = inputs.Linear("split2", M, K, N)
+    x, w, dy = (inputs.random_bf16(s, seed=sd, std=st) for s, sd, st in
+                (((M, K), 17, 1.0), ((N, K), 18, K ** -0.5), ((M, N), 19, 1e-3 ** 0.5)))
+    buf = f8.LinearBuffers(M, N, K, DEV)
+    buf.forward(x.to(DEV), w.to(DEV), "dynamic", "twopass")
+    ref = oracle.linear_step(bits(x), bits(w), bits(dy), gemms=False)
+    for nbytes in (full // 2, 0):
+        print(f"split scratch {nbytes} of {full} bytes", flush=True)
+        buf.gemm_ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV) if nbytes else None
+        buf.backward(dy.to(DEV), "dynamic", "twopass")
+        torch.cuda.synchronize()
+        _check_gemms(buf, ref, lin, seed=5)
