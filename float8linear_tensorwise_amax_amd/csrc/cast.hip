@@ -27,8 +27,10 @@
 // Delayed mode also folds max |x| into state.amax (atomic max on the fp32
 // bit pattern, which orders like the value for non-negative floats).  Same-
 // address atomics serialise (one per tile cost 6-16 us per cast at 1248-5450
-// tiles, measured), so a delayed-mode workgroup takes four tiles -- four
-// independent 256-thread quarters, each as above -- and issues one atomic.
+// tiles, measured), so a delayed-mode workgroup takes two tiles -- two
+// independent 256-thread halves, each as above -- and issues one atomic (two
+// tiles beat four by 12-16% at 1248-4800 tiles, where four leave a coarse
+// last wave of workgroups; the same elsewhere).
 //
 // HBM-bound: 2 bytes read + 2 bytes written per element (4 B/elem).
 #include "device_common.h"
@@ -84,8 +86,8 @@ struct CastJobs {
   int count;
 };
 
-// TPW tiles per workgroup: thread quarter `sub` (256 threads) casts tile
-// first_tile + sub; a quarter past the tensor's last tile loads and stores
+// TPW tiles per workgroup: the 256 threads of part `sub` cast tile
+// first_tile + sub; a part past the tensor's last tile loads and stores
 // nothing.
 template <int FMT, int MODE, bool WRITE_T, int TPW>
 __global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const CastJobs jobs) {
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const Ca
   uint8_t *__restrict__ q = jb.q;
   uint8_t *__restrict__ qt = jb.qt;
   const int sub = TPW > 1 ? (int)(threadIdx.x / kThreads) : 0;
-  const int local = ((int)blockIdx.x - jb.first) * TPW + sub;  // this quarter's tile
+  const int local = ((int)blockIdx.x - jb.first) * TPW + sub;  // this part's tile
   const bool live = TPW == 1 || local < jb.ntiles;
   uint32_t *tile = tiles_lds[sub];
 
@@ -308,10 +310,10 @@ __global__ __launch_bounds__(kDbCols * kDbGroups) void dbias_kernel(const float 
   }
 }
 
-// Tiles per workgroup: four in delayed mode (one atomic per four tiles),
-// one in dynamic mode.
+// Tiles per workgroup: two in delayed mode (one atomic per two tiles), one
+// in dynamic mode.
 template <int MODE>
-constexpr int tiles_per_wg() { return MODE == F8LIN_DELAYED ? 4 : 1; }
+constexpr int tiles_per_wg() { return MODE == F8LIN_DELAYED ? 2 : 1; }
 
 template <int FMT, int MODE>
 void launch_ct(unsigned grid, const CastJobs &jobs, bool write_t, hipStream_t stream) {
