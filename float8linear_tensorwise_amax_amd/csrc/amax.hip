@@ -2,9 +2,11 @@
 // REDUCTION kernel_algo rows of the single-linear-layer table in
 // pytorch/torchtitan PR #778):
 //   atomic : one launch; each workgroup reduces its grid-stride share and folds
-//            it into one device-wide slot with an atomic max; the last
-//            workgroup to finish (ticket counter) publishes the result and
-//            clears the slot and ticket for the next call.
+//            it with an atomic max into the slot of its group (workgroup
+//            index mod 8); the last workgroup of a group (ticket counter)
+//            folds the group into the tensor's slot the same way, and the
+//            last group to do so publishes the result.  Every slot and
+//            ticket is cleared again for the next call.
 //   twopass: the same per-workgroup reduction writes one partial per
 //            workgroup; the second pass reduces them -- inside the prologue of
 //            the cast kernel that consumes the amax (f8lin_forward /
@@ -19,7 +21,8 @@
 // workgroup per CU (256) per tensor, striding over the tensor: on MI355X
 // device-wide atomics on one address are serialised beyond the per-XCD L2s
 // (about 10 ns each, measured), so the atomic variant keeps the number of
-// workgroups -- and with it the serialised tail of atomics -- small.  Fewer,
+// workgroups small and spreads their atomics over eight group slots, one
+// 128-byte line each (eight-way less serialisation per address).  Fewer,
 // fuller waves start sooner than many short ones (measured: 512 threads x 16
 // loads beat 1024 x 8 by 4-6% on 64-512 MiB tensors).  Loads are ordinary
 // (cached): the cast that follows re-reads the same tensor and can hit in the
@@ -103,24 +106,42 @@ __device__ __forceinline__ int job_of(const AmaxJobs &jobs) {
   return t;
 }
 
+// Folds m into slot [0] (running max) and takes a ticket from slot [1]; true
+// for the last of `members` callers, which gets the slot's final max in
+// `all` and leaves the slot cleared.
+//
+// No fence: device-scope atomics are performed at one coherence point, and a
+// fence here (an L2 write-back plus invalidate of the whole XCD cache on this
+// chip) cost more than the reduction itself.  The order that matters -- each
+// caller's max performed before its ticket -- comes from a data dependency
+// instead: the ticket's operand uses the value the max returned, so it cannot
+// issue before the max has completed.  Slot values are 15-bit magnitudes, so
+// prev >> 15 is always 0 and the ticket adds exactly 1.  The last caller
+// reads and clears the max with one exchange, issued only after its ticket
+// came back, so every member's max is in.
+__device__ __forceinline__ bool fold_last(uint32_t *slot, uint32_t m, uint32_t members, uint32_t &all) {
+  const uint32_t prev = atomicMax(&slot[0], m);
+  if (atomicAdd(&slot[1], 1u + (prev >> 15)) != members - 1) return false;
+  all = atomicExch(&slot[0], 0u);
+  atomicExch(&slot[1], 0u);
+  return true;
+}
+
 __global__ __launch_bounds__(kThreads) void amax_atomic_kernel(const AmaxJobs jobs, uint32_t *ws) {
   const int t = job_of(jobs);
   const AmaxJob &jb = jobs.j[t];
   const int64_t nthreads = (int64_t)jb.grid * kThreads;
-  const int64_t gtid = (int64_t)(blockIdx.x - jb.first) * kThreads + threadIdx.x;
+  const int lb = (int)blockIdx.x - jb.first;
+  const int64_t gtid = (int64_t)lb * kThreads + threadIdx.x;
   const uint32_t m = block_max(thread_magmax(jb.x, jb.n, gtid, nthreads));
   if (threadIdx.x == 0) {
-    uint32_t *slot = ws + kWsSlotWords * t;  // [0] running max, [1] ticket
-    atomicMax(&slot[0], m);
-    __threadfence();
-    const uint32_t ticket = atomicAdd(&slot[1], 1u);
-    if (ticket == (uint32_t)jb.grid - 1) {  // every other workgroup of this tensor has folded its max in
-      __threadfence();
-      const uint32_t all = atomicMax(&slot[0], 0u);  // atomic read of the final max
+    const int grp = lb % kAmaxGroups;
+    const uint32_t members = (uint32_t)((jb.grid - grp + kAmaxGroups - 1) / kAmaxGroups);
+    const uint32_t groups = (uint32_t)min(jb.grid, kAmaxGroups);
+    uint32_t gm, all;
+    if (fold_last(ws + kWsGroupOffset + kWsSlotWords * (kAmaxGroups * t + grp), m, members, gm) &&
+        fold_last(ws + kWsSlotWords * t, gm, groups, all))
       jb.out[0] = __uint_as_float(all << 16);
-      atomicExch(&slot[0], 0u);
-      atomicExch(&slot[1], 0u);
-    }
   }
 }
 

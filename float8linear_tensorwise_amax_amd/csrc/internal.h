@@ -11,12 +11,18 @@ namespace f8lin {
 
 // Workspace layout (uint32 words): for tensor t of a launch, words
 // [kWsSlotWords*t, +2) hold the atomic variant's running max and ticket;
-// words [kWsPartialsOffset + kMaxGrid*t, +kMaxGrid) the two-pass partials.
+// words [kWsPartialsOffset + kMaxGrid*t, +kMaxGrid) the two-pass partials;
+// words [kWsGroupOffset + kWsSlotWords*(kAmaxGroups*t + g), +2) the atomic
+// variant's group g running max and ticket (one 128-byte line each).
 constexpr int kMaxAmaxTensors = 2;
 constexpr int kMaxGrid = 256;  // amax workgroups per tensor: one per CU
 constexpr int kWsSlotWords = 32;
 constexpr int kWsPartialsOffset = 64;
+constexpr int kAmaxGroups = 8;
+constexpr int kWsGroupOffset = kWsPartialsOffset + kMaxGrid * kMaxAmaxTensors;
 constexpr size_t kWorkspaceBytes = 8192;
+static_assert((kWsGroupOffset + kWsSlotWords * kAmaxGroups * kMaxAmaxTensors) * 4 <= (int)kWorkspaceBytes,
+              "workspace layout");
 
 struct AmaxTensor {
   const uint16_t *x;

@@ -71,8 +71,10 @@ typedef enum {
 typedef enum { F8LIN_E4M3 = 0, F8LIN_E5M2 = 1 } f8lin_fmt;
 
 /* The two amax algorithms of the single-linear benchmark (PR #778 table):
- * ATOMIC: every workgroup reduces its share and folds it into one global
- *         slot with an atomic max (one launch).
+ * ATOMIC: every workgroup reduces its share and folds it with an atomic
+ *         max into one of eight group slots; the last workgroup of a group
+ *         folds the group into the tensor's slot, and the last group
+ *         publishes the amax (one launch, no fences).
  * TWOPASS: every workgroup writes its partial max; a second one-workgroup
  *          launch reduces the partials. */
 typedef enum { F8LIN_AMAX_ATOMIC = 0, F8LIN_AMAX_TWOPASS = 1 } f8lin_amax_algo;
