@@ -36,7 +36,9 @@ def _amax_gpu(f8, x_dev, algo):
 # ------------------------------------------------------------------ amax
 
 @pytest.mark.parametrize("algo", ["atomic", "twopass"])
-@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4095, 65536, 1_000_003, 16 * 4096 * 4 + 5, 64 * 1024 * 1024 + 24])
+# 851_171 elements take 13 workgroups: the atomic fold's eight group slots get two members or one
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 4095, 65536, 851_171, 1_000_003, 16 * 4096 * 4 + 5,
+                               64 * 1024 * 1024 + 24])
 def test_amax_matches_oracle(f8, algo, n):
     print(f"amax algo={algo} n={n}", flush=True)
     x = inputs.random_bf16((n,), seed=n, std=3.0)
