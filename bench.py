@@ -65,9 +65,10 @@ def sha256_of(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(gemm_src):
+def load_traffic(gemm_src, workload):
     """HBM traffic of the GEMM from rocprofv3 counter runs, if the committed
-    record was taken on the current kernel source (else None)."""
+    record was taken on the current kernel source and on this workload (else
+    None)."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -75,7 +76,7 @@ def load_traffic(gemm_src):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sha256_of(gemm_src):
+    if rec.get("source_sha256") != sha256_of(gemm_src) or rec.get("workload_name") != workload:
         return None
     return rec
 
@@ -218,15 +219,16 @@ def main():
         out.update(instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed))
         # the step's dominant kernel: the backward's dgrad + wgrad launch
         rl = out["kernels"]["gemm_bwd_pair"]
-        traffic = load_traffic(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "csrc", "gemm.hip"))
+        traffic = load_traffic(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "csrc", "gemm.hip"),
+                               args.workload)
         out["roofline"] = {"kernel": "gemm_fp8_tn_kernel<e5m2,e4m3> (dgrad + wgrad, one launch)",
                            "bound": "mfma", "achieved": rl["tflops"],
                            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(rl["tflops"] / PEAK_FP8_TFLOPS, 4),
-                           "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None)}
+                           "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None),
+                           "algorithmic_bytes_per_launch": rl["algorithmic_bytes_per_launch"]}
         if traffic:
             out["roofline"]["traffic_note"] = traffic.get("note", "")
-            out["roofline"]["algorithmic_bytes_per_launch"] = rl["algorithmic_bytes_per_launch"]
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, wl, sets, np, torch)
