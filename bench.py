@@ -241,7 +241,13 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
     GEMM launch again on its own (f8lin_gemm; f8lin_gemm_batch for the
     backward's dgrad + wgrad pair).  A call's time minus its GEMM's is its
     amax + cast phase, whose algorithmic bytes are 2 B/element for each
-    dynamic-mode amax pass and 4 B/element for each cast."""
+    dynamic-mode amax pass and 4 B/element for each cast.  f8lin_gemm_batch
+    is the plain shared launch: where f8lin_backward splits a GEMM along K or
+    hands out the pair's tiles through its work queue (problems of different
+    contraction length), the pair inside the call runs faster than this
+    figure and the amax + cast share absorbs the difference; the step time
+    above is the real path either way.  At M = N = K the two launches are the
+    same."""
     acc = {k: [0.0, 0, 0.0] for k in ("fwd_call", "bwd_call", "gemm_fwd", "gemm_bwd_pair")}  # ms, calls, units
     ew_bytes = {"fwd": 0, "bwd": 0}
     gemm_bytes = {"gemm_fwd": [], "gemm_bwd_pair": []}

@@ -363,8 +363,11 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
   const int64_t gemm_ws = a.gemm_ws ? (int64_t)std::min<size_t>(a.gemm_ws_bytes,
                                                                  f8lin_backward_gemm_workspace_bytes(a.M, a.N, a.K))
                                     : 0;
+  // dynamic mode needs the workspace for the amax; in either mode a valid one
+  // also carries the GEMM's work queue (delayed mode may pass none)
   const bool need_ws = a.mode_dy == F8LIN_DYNAMIC;
   if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
+  const bool use_ws = need_ws || check_ws(a.ws, a.ws_bytes) == F8LIN_OK;
   const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
   if (db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
   const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
@@ -374,7 +377,7 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
                           {a.dy8t, mn},
                           {a.sdy.scale, 8},
                           {a.sdy.amax, 4},
-                          {a.ws, need_ws ? (int64_t)kWorkspaceBytes : 0},
+                          {a.ws, use_ws ? (int64_t)kWorkspaceBytes : 0},
                           {a.dbias, a.dbias ? 2 * a.N : 0},
                           {a.dbias_ws, db_ws},
                           {a.gemm_ws, gemm_ws}};
@@ -400,7 +403,8 @@ int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
   //   dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
   const GemmDesc g[2] = {{a.dy8, a.w8t, a.sdy.scale + 1, a.sw.scale + 1, a.dx, a.M, a.K, a.N},
                          {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
-  return status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws));
+  return status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws,
+                                use_ws ? ws + kWsQueueOffset : nullptr));
 }
 
 int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream) {

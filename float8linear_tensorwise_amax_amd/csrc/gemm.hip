@@ -58,6 +58,8 @@
 //     v_cvt_pk_bf16_f32 (nearest even; checked against a software rounding on
 //     all 2^32 binary32 patterns), staged through LDS per wave and written as
 //     16-byte row segments.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -88,7 +90,8 @@ struct Problem {
 struct Batch {
   Problem p[kMaxGemms];
   int count;
-  int nt_stores;  // write C with non-temporal stores (many tiles per CU)
+  int nt_stores;     // write C with non-temporal stores (many tiles per CU)
+  uint32_t *queue;   // DYN: per-XCD work-queue words (zero at launch, left zero)
 };
 
 __device__ __forceinline__ int slot128(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
@@ -111,7 +114,12 @@ using bool_t = std::integral_constant<bool, B>;
 // blocks; the tile list holds every (range, tile) pair, and a tile writes its
 // range's fp32 partial product, unscaled, to slab `range` of P.c (summed,
 // scaled and rounded by split_reduce_kernel).
-template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool PARTIAL>
+// DYN: the XCD's workgroups take the items of its list from a counter (one
+// atomic per tile) instead of every wx-th one; the host puts the problem
+// with the most K blocks first.  With problems of very different K (dgrad
+// over N next to wgrad over the token count) a fixed stride hands a few
+// workgroups the long tiles on top of their share of short ones.
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool PARTIAL, bool DYN = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const Batch batch) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
@@ -122,9 +130,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   constexpr int LQ = LA + LB;
   constexpr int RB = WTN * 2;  // bytes per staged output row
   static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 2, "tile configuration");
+  static_assert(!(DYN && PARTIAL), "split problems keep the fixed stride");
   static_assert(LQ <= 15, "vmcnt immediate");
   static_assert(NW * WTM * RB <= 2 * STB, "epilogue staging must fit in LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB];
+  // two stages of A and B (the epilogue reuses them for its staging); DYN
+  // also keeps its two next-item slots past them, in the same array
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB + (DYN ? 16 : 0)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;  // K half within a 64-byte sub-step
@@ -146,7 +157,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     total += len[i];
   }
 
-  for (int it = local_wg; it < total; it += wx) {
+  // DYN: item wx + i goes to the workgroup whose fetch returned i.  Thread 0
+  // fetches at the start of a tile and publishes the value in next_item[par]
+  // once its tile's first copies are in; every thread reads it after the
+  // tile's last barrier.  Two slots, alternating per tile: the write of a
+  // slot and the previous read of it are always a barrier apart.  The fetch
+  // is written as an instruction of its own because the compiler would
+  // otherwise wait for its result at once -- and with it, vmcnt being in
+  // order, for the previous tile's output stores; issued before the tile's
+  // copies, it is complete once the prologue's wait for block 0 returns.
+  int *const next_item = reinterpret_cast<int *>(smem + 2 * STB);
+  int par = 0;
+  uint32_t *const queue = DYN ? batch.queue + xcd * kQueueWords : nullptr;
+  for (int it = local_wg; it < total;) {
+    uint32_t fetched = 0;
+    if constexpr (DYN) {
+      if (tid == 0) asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(fetched) : "v"(queue), "v"(1u) : "memory");
+    }
+    auto publish = [&]() {
+      if constexpr (DYN) {
+        if (tid == 0) next_item[par] = (int)fetched + wx;
+      }
+    };
     // problem pi, tile t of it: this XCD's shares of the problems follow one another
     int pi = 0, off = it;
 #pragma unroll
@@ -308,6 +340,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       }
       __builtin_amdgcn_s_barrier();
+      publish();
 #pragma unroll
       for (int j = 0; j < TN; ++j) fb[j] = rd(0, OPA, brow[j], 0);
 #pragma unroll
@@ -317,6 +350,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (; s + 2 < nk; ++s) block(s, bool_t<true>(), bool_t<true>());
       if (s + 1 < nk) block(s++, bool_t<true>(), bool_t<false>());
       block(s, bool_t<false>(), bool_t<false>());
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the fetch has returned
+      publish();
     }
 
     if constexpr (PARTIAL) {
@@ -341,6 +377,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
           }
         }
       __syncthreads();  // every wave is done with the stage buffers before the next tile's copies
+      it += wx;
       continue;
     }
 
@@ -410,6 +447,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 0);
     }
     __syncthreads();  // staging reads done before the next tile's copies land
+    if constexpr (DYN) {
+      it = __builtin_amdgcn_readfirstlane(next_item[par]);
+      par ^= 1;
+    } else {
+      it += wx;
+    }
+  }
+  if constexpr (DYN) {
+    // The last of the XCD's workgroups to get here clears its queue words.
+    // Each workgroup's fetches have all returned (the last one ended its
+    // loop) before it takes this ticket, so none can follow the clear.
+    if (tid == 0 && atomicAdd(queue + 1, 1u) == (uint32_t)wx - 1) {
+      atomicExch(queue, 0u);
+      atomicExch(queue + 1, 0u);
+    }
   }
 }
 
@@ -519,7 +571,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 }
 
 template <int FA, int FB>
-void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, hipStream_t stream) {
+void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, hipStream_t stream) {
   // skinny problems get their own launches; problems with few long tiles are
   // split along K when there is room for their partials; the rest share one
   Batch rest{}, split{};
@@ -570,7 +622,17 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, hipStream_t strea
     // lines from the caches: stream it (measured: -3.5% time at 65536 x 4096 x
     // 4096, +2% at 4096^3 where each CU writes one tile).
     rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
-    if (use_big) {
+    // Problems whose tiles contract over different numbers of K blocks take
+    // their tiles from a work queue, the longest problem first.
+    bool mixed = false;
+    for (int i = 1; i < rest.count; ++i)
+      mixed |= (rest.p[i].K + kBK - 1) / kBK != (rest.p[0].K + kBK - 1) / kBK;
+    if (use_big && mixed && queue) {
+      std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
+      rest.queue = queue;
+      gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, false, true>
+          <<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(rest);
+    } else if (use_big) {
       gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, false>
           <<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(rest);
     } else {
@@ -607,7 +669,7 @@ size_t split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream, void *split_ws,
-                        size_t split_bytes) {
+                        size_t split_bytes, uint32_t *queue) {
   Batch b{};
   for (int i = 0; i < count; ++i) {
     if (d[i].M == 0 || d[i].N == 0) continue;
@@ -626,13 +688,13 @@ hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipS
   if (b.count == 0) return hipSuccess;
   float *ws = reinterpret_cast<float *>(split_ws);
   if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E4M3)
-    launch_fmt<0, 0>(b, ws, split_bytes, stream);
+    launch_fmt<0, 0>(b, ws, split_bytes, queue, stream);
   else if (fmt_a == F8LIN_E5M2 && fmt_b == F8LIN_E4M3)
-    launch_fmt<1, 0>(b, ws, split_bytes, stream);
+    launch_fmt<1, 0>(b, ws, split_bytes, queue, stream);
   else if (fmt_a == F8LIN_E4M3 && fmt_b == F8LIN_E5M2)
-    launch_fmt<0, 1>(b, ws, split_bytes, stream);
+    launch_fmt<0, 1>(b, ws, split_bytes, queue, stream);
   else
-    launch_fmt<1, 1>(b, ws, split_bytes, stream);
+    launch_fmt<1, 1>(b, ws, split_bytes, queue, stream);
   return hipGetLastError();
 }
 

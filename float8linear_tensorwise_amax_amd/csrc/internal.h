@@ -13,16 +13,19 @@ namespace f8lin {
 // [kWsSlotWords*t, +2) hold the atomic variant's running max and ticket;
 // words [kWsPartialsOffset + kMaxGrid*t, +kMaxGrid) the two-pass partials;
 // words [kWsGroupOffset + kWsSlotWords*(kAmaxGroups*t + g), +2) the atomic
-// variant's group g running max and ticket (one 128-byte line each).
+// variant's group g running max and ticket (one 128-byte line each);
+// words [kWsQueueOffset + kQueueWords*x, +2) the backward GEMM's work-queue
+// counter and done ticket of XCD x (one line each).
 constexpr int kMaxAmaxTensors = 2;
 constexpr int kMaxGrid = 256;  // amax workgroups per tensor: one per CU
 constexpr int kWsSlotWords = 32;
 constexpr int kWsPartialsOffset = 64;
 constexpr int kAmaxGroups = 8;
 constexpr int kWsGroupOffset = kWsPartialsOffset + kMaxGrid * kMaxAmaxTensors;
+constexpr int kQueueWords = 32;
+constexpr int kWsQueueOffset = kWsGroupOffset + kWsSlotWords * kAmaxGroups * kMaxAmaxTensors;
 constexpr size_t kWorkspaceBytes = 8192;
-static_assert((kWsGroupOffset + kWsSlotWords * kAmaxGroups * kMaxAmaxTensors) * 4 <= (int)kWorkspaceBytes,
-              "workspace layout");
+static_assert((kWsQueueOffset + kQueueWords * 8) * 4 <= (int)kWorkspaceBytes, "workspace layout");
 
 struct AmaxTensor {
   const uint16_t *x;
@@ -75,8 +78,10 @@ struct GemmDesc {
 // split_ws (optional, 16-byte aligned): room for the fp32 partial products of
 // problems split along K (split_factor > 1); a problem that does not fit
 // runs unsplit.  Contents need no initialisation.
+// queue (optional): the workspace's work-queue words (zero; left zero), with
+// which problems of different K share a launch through a work queue.
 hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipStream_t stream,
-                        void *split_ws = nullptr, size_t split_bytes = 0);
+                        void *split_ws = nullptr, size_t split_bytes = 0, uint32_t *queue = nullptr);
 // K ranges a problem is split into when a partial-product workspace is given
 // (1: not split), and the bytes its partials need.
 int split_factor(int64_t M, int64_t N, int64_t K);

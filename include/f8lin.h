@@ -104,7 +104,8 @@ typedef struct {
 /* Bytes of device workspace that f8lin_amax / f8lin_forward /
  * f8lin_backward need (a constant).  The caller zero-fills it once before
  * first use.  Every call leaves the words that must start at zero (the
- * atomic algorithm's running max and ticket) at zero again; f8lin_amax
+ * atomic algorithm's running maxima and tickets, the backward GEMM's
+ * work-queue counters) at zero again; f8lin_amax
  * leaves the whole workspace zero-filled, while f8lin_forward /
  * f8lin_backward with the two-pass algorithm leave its partial maxima in
  * the workspace (every call overwrites them before reading them). */
@@ -202,7 +203,12 @@ typedef struct {
  * K ranges whose fp32 partial products a second kernel sums in range order
  * (the same bits on every run), scales and rounds to bf16.  The summation
  * order differs from the unsplit GEMM's, so the results may differ from it
- * in the last bits, within the GEMM tolerance. */
+ * in the last bits, within the GEMM tolerance.
+ * ws: required in dynamic mode (the amax); optional in delayed mode.  A
+ * valid workspace (either mode) also holds the work-queue counters through
+ * which dgrad and wgrad share their launch when their contraction lengths
+ * differ; without one (delayed mode, ws NULL) they share it with a fixed
+ * tile order -- the same results, bit for bit. */
 typedef struct {
   int64_t M, N, K;
   const uint16_t *dy;           /* input (M, N) */

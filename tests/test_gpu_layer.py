@@ -324,3 +324,34 @@ def test_backward_split_workspace_too_small_for_both(f8):
         buf.backward(dy.to(DEV), "dynamic", "twopass")
         torch.cuda.synchronize()
         _check_gemms(buf, ref, lin, seed=5)
+
+
+def test_backward_work_queue_matches_the_fixed_order(f8):
+    """dgrad and wgrad of different contraction lengths (dX over N = 1024,
+    dW over 8192 tokens) share their launch through the workspace's work
+    queue.  The outputs are the same bits as the plain shared launch
+    (f8lin_gemm_batch, fixed tile order) on the same fp8 operands, on every
+    one of three calls in a row (the queue is reset between them), the
+    workspace is all zero again after each call (atomic amax: nothing else
+    is left in it), and the outputs meet the GEMM tolerance."""
+    M, N, K = 8192, 1024, 4096
+    lin = inputs.Linear("queue", M, K, N)
+    x, w, dy = (inputs.random_bf16(s, seed=sd, std=st) for s, sd, st in
+                (((M, K), 27, 1.0), ((N, K), 28, K ** -0.5), ((M, N), 29, 1e-3 ** 0.5)))
+    buf = f8.LinearBuffers(M, N, K, DEV)
+    buf.gemm_ws = None  # no split: both GEMMs go to the shared launch
+    buf.forward(x.to(DEV), w.to(DEV), "dynamic", "atomic")
+    dx_ref = torch.empty_like(buf.dx)
+    dw_ref = torch.empty_like(buf.dw)
+    for call in range(3):
+        print(f"work-queue backward call {call}", flush=True)
+        buf.backward(dy.to(DEV), "dynamic", "atomic")
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(buf.ws).item() == 0, "workspace not left zero"
+        f8.gemm_batch([(buf.dy8, buf.w8t, buf.sdy.inv_scale, buf.sw.inv_scale, dx_ref),
+                       (buf.dy8t, buf.x8t, buf.sdy.inv_scale, buf.sx.inv_scale, dw_ref)], "e5m2", "e4m3")
+        torch.cuda.synchronize()
+        assert torch.equal(buf.dx.view(torch.int16), dx_ref.view(torch.int16)), f"dX differs, call {call}"
+        assert torch.equal(buf.dw.view(torch.int16), dw_ref.view(torch.int16)), f"dW differs, call {call}"
+    ref = oracle.linear_step(bits(x), bits(w), bits(dy), gemms=False)
+    _check_gemms(buf, ref, lin, seed=31)
