@@ -143,7 +143,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
 
   // This workgroup's share of the tiles: XCD x owns a contiguous 1/8 of each
   // problem's tile list (so problems of different K stay balanced across
-  // XCDs), and its wx workgroups take every wx-th tile of that share.
+  // XCDs), and its wx workgroups take every wx-th tile of that share (DYN:
+  // the first wx in order, the rest from the XCD's counter).
   const int xcd = (int)blockIdx.x % kXcds, local_wg = (int)blockIdx.x / kXcds;
   const int nwg = (int)gridDim.x;
   const int wx = nwg / kXcds + (xcd < nwg % kXcds ? 1 : 0);
