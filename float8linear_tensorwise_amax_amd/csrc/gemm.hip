@@ -19,7 +19,9 @@
 //       big   256 x 256 tile, 8 waves (2 x 4), wave tile 128 x 64
 //             (128 fp32 accumulators per lane), one workgroup per CU;
 //       small 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64, two per CU,
-//             for problems with too few big tiles to fill 256 CUs.
+//             for problems with too few big tiles to fill 256 CUs, or
+//             whose ragged edge would leave the last round of big tiles
+//             nearly empty.
 //   * K block of 128 bytes in two LDS stages.  Global -> LDS copies use
 //     buffer_load_dwordx4 ... lds (no register staging); eight lanes fetch
 //     one full 128-byte row line (64-byte row segments, i.e. K blocks of 64,
@@ -607,9 +609,25 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(split);
   }
   if (rest.count > 0) {
-    int64_t big = 0;
-    for (int i = 0; i < rest.count; ++i) big += (int64_t)((rest.p[i].M + 255) / 256) * ((rest.p[i].N + 255) / 256);
-    const bool use_big = big >= kCUs;
+    int64_t big = 0, small = 0;
+    for (int i = 0; i < rest.count; ++i) {
+      big += (int64_t)((rest.p[i].M + 255) / 256) * ((rest.p[i].N + 255) / 256);
+      small += (int64_t)((rest.p[i].M + 127) / 128) * ((rest.p[i].N + 127) / 128);
+    }
+    // Problems whose tiles contract over different numbers of K blocks take
+    // their tiles from a work queue, the longest problem first.
+    bool mixed = false;
+    for (int i = 1; i < rest.count; ++i)
+      mixed |= (rest.p[i].K + kBK - 1) / kBK != (rest.p[0].K + kBK - 1) / kBK;
+    // Big tiles, unless a ragged edge leaves their last round nearly empty.
+    // At equal K a round of small tiles (two per CU) costs ~0.57 of a round of
+    // big ones (4096^3: one big round 55.7 us, two small rounds 64.0 us), so
+    // the small tiles win when 0.6 x their rounds < the big rounds
+    // (12288 x 1600 x 1600: 336 big tiles in two rounds 46.5 us, 1248 small
+    // ones in three 43.0 us; 12288 x 4800 x 1600: four big rounds 99.4 us,
+    // eight small ones 113 us).  A queued batch keeps the big tiles.
+    const int64_t big_rounds = (big + kCUs - 1) / kCUs, small_rounds = (small + 2 * kCUs - 1) / (2 * kCUs);
+    const bool use_big = big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
     const int bm = use_big ? 256 : 128;
     int tiles = 0;
     for (int i = 0; i < rest.count; ++i) {
@@ -623,11 +641,6 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     // lines from the caches: stream it (measured: -3.5% time at 65536 x 4096 x
     // 4096, +2% at 4096^3 where each CU writes one tile).
     rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
-    // Problems whose tiles contract over different numbers of K blocks take
-    // their tiles from a work queue, the longest problem first.
-    bool mixed = false;
-    for (int i = 1; i < rest.count; ++i)
-      mixed |= (rest.p[i].K + kBK - 1) / kBK != (rest.p[0].K + kBK - 1) / kBK;
     if (use_big && mixed && queue) {
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;
