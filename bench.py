@@ -136,8 +136,6 @@ def main():
                 buf, (l, x, w, dy) = bufs[g[0]], data[g[0]]
                 buf.forward(x, w, mode, algo)
                 buf.backward(dy, mode, algo)
-                if delayed:
-                    f8lin.delayed_update(buf.states())
                 continue
             # linears reading one X: X cast once, their forward GEMMs in one launch
             lead = bufs[g[0]]
@@ -149,6 +147,9 @@ def main():
                 b = bufs[i]
                 f8lin.backward(data[i][3], lead.x8t, b.w8t, b.dx, b.dw, b.dy8, b.dy8t, lead.sx, b.sw, b.sdy, b.ws,
                                mode, algo)
+        if delayed:
+            # the history sync after backward: one call for every linear's states
+            f8lin.delayed_update([st for b in bufs for st in b.states()])
 
     def timed_steps(algo):
         for t in range(args.warmup):
