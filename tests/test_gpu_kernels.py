@@ -212,7 +212,10 @@ def _gemm_gpu(f8, a, fa, b, fb, inv_a, inv_b):
 
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 @pytest.mark.parametrize("mnk", [(16, 16, 16), (32, 48, 64), (128, 128, 128), (144, 272, 400), (16, 4096, 4096),
-                                 (256, 4800, 1600), (4096, 16, 16), (1024, 1024, 4096), (64, 80, 16)])
+                                 (256, 4800, 1600), (4096, 16, 16), (1024, 1024, 4096), (64, 80, 16),
+                                 # 256x256 tiles with a ragged last K block: 64 bytes (its all-zero
+                                 # second half skipped) and 80 bytes (not skipped)
+                                 (4096, 4096, 1600), (8192, 2048, 208)])
 def test_gemm_matches_oracle(f8, fa, fb, mnk):
     M, N, K = mnk
     print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
