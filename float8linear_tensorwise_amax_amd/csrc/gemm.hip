@@ -164,19 +164,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   // fetches at the start of a tile and publishes the value in next_item[par]
   // once its tile's first copies are in; every thread reads it after the
   // tile's last barrier.  Two slots, alternating per tile: the write of a
-  // slot and the previous read of it are always a barrier apart.  The fetch
-  // is written as an instruction of its own because the compiler would
-  // otherwise wait for its result at once -- and with it, vmcnt being in
-  // order, for the previous tile's output stores; issued before the tile's
-  // copies, it is complete once the prologue's wait for block 0 returns.
+  // slot and the previous read of it are always a barrier apart.  Every
+  // thread issues the fetch, so that it sits under no branch: where a branch
+  // joins, the compiler would wait for the result at once -- and, vmcnt
+  // being in order, for the previous tile's output stores.  It is a buffer
+  // atomic on the XCD's one-word counter, and only thread 0's offset lies
+  // inside that range: the range check discards every other lane's add.
+  // Issued before the tile's copies, it has returned once the prologue's
+  // wait for block 0 does, so its use there costs no wait of its own.
   int *const next_item = reinterpret_cast<int *>(smem + 2 * STB);
   int par = 0;
   uint32_t *const queue = DYN ? batch.queue + xcd * kQueueWords : nullptr;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void *)queue, (short)0, 4, 0x00020000);
   for (int it = local_wg; it < total;) {
     uint32_t fetched = 0;
-    if constexpr (DYN) {
-      if (tid == 0) asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(fetched) : "v"(queue), "v"(1u) : "memory");
-    }
+    if constexpr (DYN) fetched = (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, qrs, tid == 0 ? 0 : kOutOfRange, 0, 0);
     auto publish = [&]() {
       if constexpr (DYN) {
         if (tid == 0) next_item[par] = (int)fetched + wx;
