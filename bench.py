@@ -230,10 +230,35 @@ def main():
                            "algorithmic_bytes_per_launch": rl["algorithmic_bytes_per_launch"]}
         if traffic:
             out["roofline"]["traffic_note"] = traffic.get("note", "")
+        out["hbm_copy_reference"] = copy_reference(torch, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, wl, sets, np, torch)
     print(json.dumps(out), flush=True)
+
+
+def copy_reference(torch, stream, nbytes=1 << 30, reps=20):
+    """The rate a plain device-to-device copy reaches (the runtime's copy
+    kernel, 1 GiB read + 1 GiB written per copy), timed with HIP events on
+    the launch stream: what this HBM delivers to a streaming kernel, beside
+    the 8 TB/s spec that the roofline fractions use.  Context only: no step
+    of the path runs through it."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    return {"what": "device-to-device copy of 1 GiB (read + write), HIP events, average of 20",
+            "us_per_copy": round(us, 2), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
