@@ -21,7 +21,10 @@
 //       small 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64, two per CU,
 //             for problems with too few big tiles to fill 256 CUs, or
 //             whose ragged edge would leave the last round of big tiles
-//             nearly empty.
+//             nearly empty;
+//       medium 64 x 128 tile, 4 waves (2 x 2), wave tile 32 x 64, when even
+//             the small tiles number fewer than the CUs (a few hundred
+//             tokens): twice as many tiles, twice as many busy CUs.
 //   * K block of 128 bytes in two LDS stages.  Global -> LDS copies use
 //     buffer_load_dwordx4 ... lds (no register staging); eight lanes fetch
 //     one full 128-byte row line (64-byte row segments, i.e. K blocks of 64,
@@ -636,12 +639,15 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     // eight small ones 113 us).  A queued batch keeps the big tiles.
     const int64_t big_rounds = (big + kCUs - 1) / kCUs, small_rounds = (small + 2 * kCUs - 1) / (2 * kCUs);
     const bool use_big = big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
-    const int bm = use_big ? 256 : 128;
+    // Fewer small tiles than CUs (e.g. 256 tokens: 64 tiles of 128 x 128):
+    // tiles of 64 x 128 occupy twice as many CUs.
+    const bool use_med = !use_big && small < kCUs;
+    const int bm = use_big ? 256 : (use_med ? 64 : 128), bn = use_big ? 256 : 128;
     int tiles = 0;
     for (int i = 0; i < rest.count; ++i) {
       Problem &p = rest.p[i];
       p.tiles_m = (p.M + bm - 1) / bm;
-      p.tiles_n = (p.N + bm - 1) / bm;
+      p.tiles_n = (p.N + bn - 1) / bn;
       p.splits = 1;
       tiles += p.tiles_m * p.tiles_n;
     }
@@ -657,6 +663,9 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     } else if (use_big) {
       gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, false>
           <<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(rest);
+    } else if (use_med) {
+      gemm_fp8_tn_kernel<FA, FB, 64, 128, 2, 2, 2, 8, false>
+          <<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(rest);
     } else {
       gemm_fp8_tn_kernel<FA, FB, 128, 128, 2, 2, 2, 8, false>
           <<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(rest);
