@@ -639,9 +639,11 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     // eight small ones 113 us).  A queued batch keeps the big tiles.
     const int64_t big_rounds = (big + kCUs - 1) / kCUs, small_rounds = (small + 2 * kCUs - 1) / (2 * kCUs);
     const bool use_big = big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
-    // Fewer small tiles than CUs (e.g. 256 tokens: 64 tiles of 128 x 128):
-    // tiles of 64 x 128 occupy twice as many CUs.
-    const bool use_med = !use_big && small < kCUs;
+    // At most one small tile per CU (e.g. 256 tokens: 64 tiles of 128 x 128):
+    // tiles of 64 x 128 occupy twice as many CUs (measured: 1024 x 4096 x
+    // 4096, 256 small tiles, 25.8 -> 24.1 us; from 384 small tiles on the
+    // small ones are faster, 2048 x 4096 x 4096 34.9 vs 46.2 us).
+    const bool use_med = !use_big && small <= kCUs;
     const int bm = use_big ? 256 : (use_med ? 64 : 128), bn = use_big ? 256 : 128;
     int tiles = 0;
     for (int i = 0; i < rest.count; ++i) {
