@@ -215,7 +215,9 @@ def _gemm_gpu(f8, a, fa, b, fb, inv_a, inv_b):
                                  (256, 4800, 1600), (4096, 16, 16), (1024, 1024, 4096), (64, 80, 16),
                                  # 256x256 tiles with a ragged last K block: 64 bytes (its all-zero
                                  # second half skipped) and 80 bytes (not skipped)
-                                 (4096, 4096, 1600), (8192, 2048, 208)])
+                                 (4096, 4096, 1600), (8192, 2048, 208),
+                                 # exactly one 128x128 tile per CU: taken by the 64x128 tiles
+                                 (1024, 4096, 256)])
 def test_gemm_matches_oracle(f8, fa, fb, mnk):
     M, N, K = mnk
     print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
