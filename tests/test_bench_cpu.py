@@ -28,3 +28,14 @@ def test_traffic_record_is_not_attached_to_other_workloads():
     b = _bench()
     for w in ("gpt1p5b_block_t12288_delayed", "linear4096_m16", "llama3_8b_layer_t8192"):
         assert b.load_traffic(GEMM_SRC, w) is None
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
