@@ -15,9 +15,9 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "device_common.h"
 #include <cstring>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace f8lin {
@@ -32,13 +32,20 @@ struct StateBatch {
   int n;
 };
 
-__global__ void delayed_update_kernel(StateBatch batch) {
+// A state is valid when it is one that pushes from the zeroed state can
+// reach: 0 <= count <= 16, 0 <= pos < 16, and pos == count until the ring
+// is full.  An invalid state (e.g. a corrupted checkpoint) is left as it is
+// and reported in status[i] (F8LIN_EINVAL; F8LIN_OK otherwise) when the
+// caller passes a status array.
+__global__ void delayed_update_kernel(StateBatch batch, int32_t *status) {
   const int i = threadIdx.x;
   if (i >= batch.n) return;
   const f8lin_state st = batch.s[i];
-  int32_t count = st.hist_meta[0];
-  int32_t pos = st.hist_meta[1];
-  pos = ((pos % kHistLen) + kHistLen) % kHistLen;
+  const int32_t count = st.hist_meta[0];
+  const int32_t pos = st.hist_meta[1];
+  const bool valid = count >= 0 && count <= kHistLen && pos >= 0 && pos < kHistLen && (count == kHistLen || pos == count);
+  if (status) status[i] = valid ? F8LIN_OK : F8LIN_EINVAL;
+  if (!valid) return;
   st.history[pos] = st.amax[0];
   st.hist_meta[1] = (pos + 1) % kHistLen;
   st.hist_meta[0] = count < kHistLen ? count + 1 : kHistLen;
@@ -91,6 +98,13 @@ int check_ws(const void *ws, size_t ws_bytes) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? F8LIN_OK : F8LIN_EHIP; }
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Records an optional timing event on the call's stream.
+int record(void *ev, hipStream_t s) {
+  return ev ? status_of(hipEventRecord((hipEvent_t)ev, s)) : F8LIN_OK;
+}
 
 #define F8_TRY(expr)                 \
   do {                               \
@@ -145,21 +159,29 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
   const int64_t M = a0.M, K = a0.K, mk = M * K;
   if (missing(a0.x, mk) || missing(a0.x8, mk) || missing(a0.x8t, mk)) return F8LIN_EINVAL;
   if (!aligned16(a0.x) || !aligned16(a0.x8) || !aligned16(a0.x8t)) return F8LIN_EALIGN;
-  bool need_ws = a0.mode_x == F8LIN_DYNAMIC;
-  Range outs[4 + 5 * kMaxGemms + 1], ins[2 + 6 * kMaxGemms];
+  // an amax of X handed in (from the producer's epilogue) replaces X's amax pass: dynamic mode only
+  const bool x_given = a0.x_amax_given != 0;
+  if (x_given && a0.mode_x != F8LIN_DYNAMIC) return F8LIN_EINVAL;
+  bool need_ws = a0.mode_x == F8LIN_DYNAMIC && !x_given;
+  Range outs[4 + 6 * kMaxGemms + 1], ins[2 + 6 * kMaxGemms];
   int no = 0, ni = 0;
   outs[no++] = {a0.x8, mk};
   outs[no++] = {a0.x8t, mk};
   outs[no++] = {a0.sx.scale, 8};
-  outs[no++] = {a0.sx.amax, 4};
+  if (x_given)
+    ins[ni++] = {a0.sx.amax, 4};
+  else
+    outs[no++] = {a0.sx.amax, 4};
   ins[ni++] = {a0.x, 2 * mk};
   ins[ni++] = {a0.sx.history, a0.mode_x == F8LIN_DELAYED ? 64 : 0};
   for (int i = 0; i < count; ++i) {
     const f8lin_fwd_args &a = list[i];
     if (i > 0 && (a.x != a0.x || a.x8 != a0.x8 || a.x8t != a0.x8t || a.M != M || a.K != K || a.mode_x != a0.mode_x ||
                   a.algo != a0.algo || a.ws != a0.ws || a.ws_bytes != a0.ws_bytes ||
-                  std::memcmp(&a.sx, &a0.sx, sizeof(f8lin_state)) != 0))
-      return F8LIN_EINVAL;  // entries must share X, its copies, its state and the workspace
+                  a.x_amax_given != a0.x_amax_given || a.ev_gemm_begin != a0.ev_gemm_begin ||
+                  a.ev_gemm_end != a0.ev_gemm_end || std::memcmp(&a.sx, &a0.sx, sizeof(f8lin_state)) != 0))
+      return F8LIN_EINVAL;  // entries must share X, its copies, its state, the workspace and the events
+    if (!aligned4(a.y_amax)) return F8LIN_EALIGN;
     const bool reuse = a.w_cast_valid != 0;
     if (reuse) {
       if (!a.sw.scale) return F8LIN_EINVAL;
@@ -175,6 +197,7 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
         !aligned16(a.bias))
       return F8LIN_EALIGN;
     outs[no++] = {a.y, 2 * mn};
+    outs[no++] = {a.y_amax, a.y_amax ? 4 : 0};
     if (reuse) {
       ins[ni++] = {a.w8, nk};
       ins[ni++] = {a.w8t, nk};
@@ -198,12 +221,18 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *ws = (uint32_t *)a0.ws;
-  // The tensors to cast, dynamic-mode ones first.
+  // The output-amax words, zeroed by the first cast launch (X is always cast).
+  ZeroWords zero;
+  for (int i = 0; i < count; ++i)
+    if (list[i].y_amax) zero.w[zero.n++] = list[i].y_amax;
+  // The tensors to cast, dynamic-mode ones first (X leads its pass).
   CastTensor ct[1 + kMaxGemms];
   int modes[1 + kMaxGemms], nt = 0;
+  bool given[1 + kMaxGemms] = {};
   for (int pass = 0; pass < 2; ++pass) {
     const int mode = pass == 0 ? F8LIN_DYNAMIC : F8LIN_DELAYED;
     if (a0.mode_x == mode) {
+      given[nt] = x_given;
       ct[nt] = CastTensor{a0.x, M, K, &a0.sx, a0.x8, a0.x8t};
       modes[nt++] = mode;
     }
@@ -219,31 +248,116 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
     const int n = (i + 1 < nt && modes[i + 1] == modes[i]) ? 2 : 1;
     CastTensor pair[2] = {ct[i], n > 1 ? ct[i + 1] : ct[i]};
     if (modes[i] == F8LIN_DYNAMIC) {
+      // amax passes for the tensors whose amax is not handed in
       AmaxTensor am[2];
-      for (int j = 0; j < n; ++j) am[j] = AmaxTensor{pair[j].x, pair[j].rows * pair[j].cols, pair[j].st->amax};
-      if (a0.algo == F8LIN_AMAX_TWOPASS) {
+      int slot[2], na = 0;
+      for (int j = 0; j < n; ++j)
+        if (!given[i + j]) {
+          slot[na] = j;
+          am[na++] = AmaxTensor{pair[j].x, pair[j].rows * pair[j].cols, pair[j].st->amax};
+        }
+      if (na > 0 && a0.algo == F8LIN_AMAX_TWOPASS) {
         const uint32_t *parts[2] = {nullptr, nullptr};
         int nparts[2] = {0, 0};
-        F8_TRY(status_of(launch_amax_partials(am, n, ws, parts, nparts, s)));
-        for (int j = 0; j < n; ++j) pair[j].partials = parts[j], pair[j].npartials = nparts[j];
-      } else {
-        F8_TRY(status_of(launch_amax(am, n, a0.algo, ws, s)));
+        F8_TRY(status_of(launch_amax_partials(am, na, ws, parts, nparts, s)));
+        for (int j = 0; j < na; ++j) pair[slot[j]].partials = parts[j], pair[slot[j]].npartials = nparts[j];
+      } else if (na > 0) {
+        F8_TRY(status_of(launch_amax(am, na, a0.algo, ws, s)));
       }
     }
-    F8_TRY(status_of(launch_cast(pair, n, F8LIN_E4M3, modes[i], s)));
+    F8_TRY(status_of(launch_cast(pair, n, F8LIN_E4M3, modes[i], s, i == 0 ? zero : ZeroWords())));
     i += n;
   }
   GemmDesc g[kMaxGemms];
   for (int i = 0; i < count; ++i) {
     const f8lin_fwd_args &a = list[i];
-    g[i] = GemmDesc{a0.x8, a.w8, a0.sx.scale + 1, a.sw.scale + 1, a.y, M, a.N, K, a.bias};
+    g[i] = GemmDesc{a0.x8, a.w8, a0.sx.scale + 1, a.sw.scale + 1, a.y, M, a.N, K, a.bias, a.y_amax};
   }
-  return status_of(launch_gemms(g, count, F8LIN_E4M3, F8LIN_E4M3, s));
+  F8_TRY(record(a0.ev_gemm_begin, s));
+  F8_TRY(status_of(launch_gemms(g, count, F8LIN_E4M3, F8LIN_E4M3, s)));
+  return record(a0.ev_gemm_end, s);
 }
 
 // Row tiles of the cast kernel: the number of per-tile column sums the bias
 // gradient reduces (one when dY has no rows: that tile's sums are zeros).
 int64_t dbias_tiles(int64_t M) { return M > 0 ? (M + kCastTile - 1) / kCastTile : 1; }
+
+// The backward: validation of every argument, then the launches.
+int backward_impl(const f8lin_bwd_args &in, void *stream) {
+  const f8lin_bwd_args a = in;
+  if (!a.sx.scale || !a.sw.scale) return F8LIN_EINVAL;
+  F8_TRY(check_mode(a.mode_dy));
+  F8_TRY(check_algo(a.algo));
+  F8_TRY(check_state(a.sdy, a.mode_dy));
+  if (bad_dim(a.M) || bad_dim(a.N) || bad_dim(a.K) || a.M * a.K > kMaxElems || a.N * a.K > kMaxElems ||
+      a.M * a.N > kMaxElems)
+    return F8LIN_ESHAPE;
+  if (missing(a.dy, a.M * a.N) || missing(a.dy8, a.M * a.N) || missing(a.dy8t, a.M * a.N) ||
+      missing(a.x8t, a.M * a.K) || missing(a.dx, a.M * a.K) || missing(a.w8t, a.N * a.K) ||
+      missing(a.dw, a.N * a.K))
+    return F8LIN_EINVAL;
+  if (!aligned16(a.dy) || !aligned16(a.x8t) || !aligned16(a.w8t) || !aligned16(a.dx) || !aligned16(a.dw) ||
+      !aligned16(a.dy8) || !aligned16(a.dy8t) || !aligned16(a.dbias) || !aligned16(a.dbias_ws) ||
+      !aligned16(a.gemm_ws))
+    return F8LIN_EALIGN;
+  // the part of gemm_ws that split GEMMs may write
+  const int64_t gemm_ws = a.gemm_ws ? (int64_t)std::min<size_t>(a.gemm_ws_bytes,
+                                                                 f8lin_backward_gemm_workspace_bytes(a.M, a.N, a.K))
+                                    : 0;
+  // dynamic mode needs the workspace for the amax; in either mode a valid one
+  // also carries the GEMM's work queue (delayed mode may pass none)
+  const bool dy_given = a.dy_amax_given != 0;
+  if (dy_given && a.mode_dy != F8LIN_DYNAMIC) return F8LIN_EINVAL;
+  if (!aligned4(a.dx_amax)) return F8LIN_EALIGN;
+  const bool need_ws = a.mode_dy == F8LIN_DYNAMIC && !dy_given;
+  if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
+  const bool use_ws = need_ws || check_ws(a.ws, a.ws_bytes) == F8LIN_OK;
+  const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
+  if (db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
+  const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
+  const Range outs[11] = {{a.dx, 2 * mk},
+                          {a.dw, 2 * nk},
+                          {a.dy8, mn},
+                          {a.dy8t, mn},
+                          {a.sdy.scale, 8},
+                          {a.sdy.amax, dy_given ? 0 : 4},
+                          {a.ws, use_ws ? (int64_t)kWorkspaceBytes : 0},
+                          {a.dbias, a.dbias ? 2 * a.N : 0},
+                          {a.dbias_ws, db_ws},
+                          {a.gemm_ws, gemm_ws},
+                          {a.dx_amax, a.dx_amax ? 4 : 0}};
+  const Range ins[7] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
+                        {a.sx.scale, 8}, {a.sw.scale, 8}, {a.sdy.history, a.mode_dy == F8LIN_DELAYED ? 64 : 0},
+                        {a.sdy.amax, dy_given ? 4 : 0}};
+  if (any_overlap(outs, 11, ins, 7)) return F8LIN_EINVAL;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *ws = (uint32_t *)a.ws;
+  CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
+  if (a.dbias) cdy.colsum = a.dbias_ws;  // the cast also sums dY's columns per 128-row tile
+  if (a.mode_dy == F8LIN_DYNAMIC && !dy_given) {
+    const AmaxTensor t = {a.dy, mn, a.sdy.amax};
+    if (a.algo == F8LIN_AMAX_TWOPASS)
+      F8_TRY(status_of(launch_amax_partials(&t, 1, ws, &cdy.partials, &cdy.npartials, s)));
+    else
+      F8_TRY(status_of(launch_amax(&t, 1, a.algo, ws, s)));
+  }
+  ZeroWords zero;
+  if (a.dx_amax) zero.w[zero.n++] = a.dx_amax;
+  F8_TRY(status_of(launch_cast(&cdy, 1, F8LIN_E5M2, a.mode_dy, s, zero)));
+  if (a.dbias) F8_TRY(status_of(launch_dbias(a.dbias_ws, dbias_tiles(a.M), a.N, a.dbias, s)));
+  // One launch for both GEMMs:
+  //   dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N;
+  //   dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
+  GemmDesc g[2] = {{a.dy8, a.w8t, a.sdy.scale + 1, a.sw.scale + 1, a.dx, a.M, a.K, a.N},
+                   {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
+  g[0].amax_out = a.dx_amax;
+  F8_TRY(record(a.ev_gemm_begin, s));
+  F8_TRY(status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws,
+                                use_ws ? ws + kWsQueueOffset : nullptr)));
+  return record(a.ev_gemm_end, s);
+}
+
 
 }  // namespace
 }  // namespace f8lin
@@ -343,76 +457,20 @@ int f8lin_forward_shared_x(const f8lin_fwd_args *args, int count, void *stream) 
 
 int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
   if (!p) return F8LIN_EINVAL;
-  const f8lin_bwd_args a = *p;
-  if (!a.sx.scale || !a.sw.scale) return F8LIN_EINVAL;
-  F8_TRY(check_mode(a.mode_dy));
-  F8_TRY(check_algo(a.algo));
-  F8_TRY(check_state(a.sdy, a.mode_dy));
-  if (bad_dim(a.M) || bad_dim(a.N) || bad_dim(a.K) || a.M * a.K > kMaxElems || a.N * a.K > kMaxElems ||
-      a.M * a.N > kMaxElems)
-    return F8LIN_ESHAPE;
-  if (missing(a.dy, a.M * a.N) || missing(a.dy8, a.M * a.N) || missing(a.dy8t, a.M * a.N) ||
-      missing(a.x8t, a.M * a.K) || missing(a.dx, a.M * a.K) || missing(a.w8t, a.N * a.K) ||
-      missing(a.dw, a.N * a.K))
-    return F8LIN_EINVAL;
-  if (!aligned16(a.dy) || !aligned16(a.x8t) || !aligned16(a.w8t) || !aligned16(a.dx) || !aligned16(a.dw) ||
-      !aligned16(a.dy8) || !aligned16(a.dy8t) || !aligned16(a.dbias) || !aligned16(a.dbias_ws) ||
-      !aligned16(a.gemm_ws))
-    return F8LIN_EALIGN;
-  // the part of gemm_ws that split GEMMs may write
-  const int64_t gemm_ws = a.gemm_ws ? (int64_t)std::min<size_t>(a.gemm_ws_bytes,
-                                                                 f8lin_backward_gemm_workspace_bytes(a.M, a.N, a.K))
-                                    : 0;
-  // dynamic mode needs the workspace for the amax; in either mode a valid one
-  // also carries the GEMM's work queue (delayed mode may pass none)
-  const bool need_ws = a.mode_dy == F8LIN_DYNAMIC;
-  if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
-  const bool use_ws = need_ws || check_ws(a.ws, a.ws_bytes) == F8LIN_OK;
-  const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
-  if (db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
-  const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
-  const Range outs[10] = {{a.dx, 2 * mk},
-                          {a.dw, 2 * nk},
-                          {a.dy8, mn},
-                          {a.dy8t, mn},
-                          {a.sdy.scale, 8},
-                          {a.sdy.amax, 4},
-                          {a.ws, use_ws ? (int64_t)kWorkspaceBytes : 0},
-                          {a.dbias, a.dbias ? 2 * a.N : 0},
-                          {a.dbias_ws, db_ws},
-                          {a.gemm_ws, gemm_ws}};
-  const Range ins[6] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
-                        {a.sx.scale, 8}, {a.sw.scale, 8}, {a.sdy.history, a.mode_dy == F8LIN_DELAYED ? 64 : 0}};
-  if (any_overlap(outs, 10, ins, 6)) return F8LIN_EINVAL;
-
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t *ws = (uint32_t *)a.ws;
-  CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
-  if (a.dbias) cdy.colsum = a.dbias_ws;  // the cast also sums dY's columns per 128-row tile
-  if (a.mode_dy == F8LIN_DYNAMIC) {
-    const AmaxTensor t = {a.dy, mn, a.sdy.amax};
-    if (a.algo == F8LIN_AMAX_TWOPASS)
-      F8_TRY(status_of(launch_amax_partials(&t, 1, ws, &cdy.partials, &cdy.npartials, s)));
-    else
-      F8_TRY(status_of(launch_amax(&t, 1, a.algo, ws, s)));
-  }
-  F8_TRY(status_of(launch_cast(&cdy, 1, F8LIN_E5M2, a.mode_dy, s)));
-  if (a.dbias) F8_TRY(status_of(launch_dbias(a.dbias_ws, dbias_tiles(a.M), a.N, a.dbias, s)));
-  // One launch for both GEMMs:
-  //   dX (M, K) = dY8 (M, N) . [W8^T (K, N)]^T : contraction over N;
-  //   dW (N, K) = dY8^T (N, M) . [X8^T (K, M)]^T : contraction over M.
-  const GemmDesc g[2] = {{a.dy8, a.w8t, a.sdy.scale + 1, a.sw.scale + 1, a.dx, a.M, a.K, a.N},
-                         {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
-  return status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws,
-                                use_ws ? ws + kWsQueueOffset : nullptr));
+  return backward_impl(*p, stream);
 }
 
-int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream) {
+int f8lin_delayed_update(const f8lin_state *states, int n_states, int32_t *status, void *stream) {
   if (!states || n_states < 0) return F8LIN_EINVAL;
+  if (!aligned4(status)) return F8LIN_EALIGN;
   for (int i = 0; i < n_states; ++i) {
     const f8lin_state &st = states[i];
     if (!st.amax || !st.history || !st.hist_meta) return F8LIN_EINVAL;
-    if (!aligned16(st.history)) return F8LIN_EALIGN;
+    if (!aligned16(st.history) || !aligned4(st.amax) || !aligned4(st.hist_meta)) return F8LIN_EALIGN;
+    // the status words are written: they must not overlap any state
+    const Range out = {status, status ? 4 * (int64_t)n_states : 0};
+    const Range st_r[3] = {{st.amax, 4}, {st.history, 64}, {st.hist_meta, 8}};
+    if (any_overlap(&out, 1, st_r, 3)) return F8LIN_EINVAL;
   }
   hipStream_t s = (hipStream_t)stream;
   for (int i0 = 0; i0 < n_states; i0 += kUpdateBatch) {
@@ -420,7 +478,7 @@ int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream) 
     memset(&b, 0, sizeof b);
     b.n = n_states - i0 < kUpdateBatch ? n_states - i0 : kUpdateBatch;
     for (int i = 0; i < b.n; ++i) b.s[i] = states[i0 + i];
-    delayed_update_kernel<<<1, 64, 0, s>>>(b);
+    delayed_update_kernel<<<1, 64, 0, s>>>(b, status ? status + i0 : nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return F8LIN_EHIP;
   }

@@ -84,6 +84,7 @@ struct CastJob {
 struct CastJobs {
   CastJob j[2];
   int count;
+  ZeroWords zero;  // set to +0 by the first workgroup
 };
 
 // TPW tiles per workgroup: the 256 threads of part `sub` cast tile
@@ -282,6 +283,7 @@ __global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const Ca
     jb.scale_out[0] = s;
     jb.scale_out[1] = 1.0f / s;
   }
+  if (blockIdx.x == 0 && threadIdx.x < (unsigned)jobs.zero.n) jobs.zero.w[threadIdx.x][0] = 0.0f;
   cast_tile(in, s);
 }
 
@@ -347,13 +349,15 @@ void launch_ct(unsigned grid, const CastJobs &jobs, bool write_t, hipStream_t st
 
 }  // namespace
 
-hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream) {
+hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream,
+                       const ZeroWords &zero) {
   // Every tensor gets at least one workgroup, even when empty: it still
   // publishes the scale.  (The C-ABI layer bounds rows * cols, so the tile
   // count fits a 1-D grid.)  The transposed copy is written for all tensors
   // of a launch or for none.
   CastJobs jobs = {};
   jobs.count = count;
+  jobs.zero = zero;
   const int64_t tpw = mode == F8LIN_DELAYED ? tiles_per_wg<F8LIN_DELAYED>() : tiles_per_wg<F8LIN_DYNAMIC>();
   int64_t total = 0;  // workgroups
   for (int i = 0; i < count; ++i) {

@@ -91,6 +91,7 @@ struct Problem {
   int M, N, K;
   int tiles_m, tiles_n;
   int splits;  // split problems: K-block ranges, each a partial product of its own
+  float *amax_out;  // AMAX: max |C| (of the rounded bf16 values) folded in here, or null
 };
 struct Batch {
   Problem p[kMaxGemms];
@@ -124,7 +125,14 @@ using bool_t = std::integral_constant<bool, B>;
 // with the most K blocks first.  With problems of very different K (dgrad
 // over N next to wgrad over the token count) a fixed stride hands a few
 // workgroups the long tiles on top of their share of short ones.
-template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool PARTIAL, bool DYN = false>
+// AMAX: the epilogue also takes max |C| over the bf16 values it stores
+// (rows < M, columns < N), so that the next layer's dynamic scaling needs
+// no amax pass over C.  A workgroup keeps one running max while it walks
+// one problem's tiles (its share of a problem is contiguous) and folds it
+// into that problem's amax_out with one atomic max when it moves on to
+// another problem or ends.
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool PARTIAL, bool DYN = false,
+          bool AMAX = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const Batch batch) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
@@ -136,11 +144,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   constexpr int RB = WTN * 2;  // bytes per staged output row
   static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 2, "tile configuration");
   static_assert(!(DYN && PARTIAL), "split problems keep the fixed stride");
+  static_assert(!(AMAX && PARTIAL), "split problems take their amax in the reduce kernel");
   static_assert(LQ <= 15, "vmcnt immediate");
   static_assert(NW * WTM * RB <= 2 * STB, "epilogue staging must fit in LDS");
   // two stages of A and B (the epilogue reuses them for its staging); DYN
-  // also keeps its two next-item slots past them, in the same array
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB + (DYN ? 16 : 0)];
+  // also keeps its two next-item slots past them and AMAX one word per wave,
+  // in the same array (a second __shared__ object makes the compiler wait
+  // for the LDS copies before every fragment read)
+  constexpr int kDynBytes = DYN ? 16 : 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB + kDynBytes + (AMAX ? 4 * NW : 0)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;  // K half within a 64-byte sub-step
@@ -177,6 +189,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   // wait for block 0 does, so its use there costs no wait of its own.
   int *const next_item = reinterpret_cast<int *>(smem + 2 * STB);
   int par = 0;
+  // AMAX: each wave's running max magnitude (15-bit bf16 field) of the
+  // values problem amax_pi's tiles stored, in LDS (red[wave], kept by lane
+  // 0: no register lives across the K loop for it); flushed by a workgroup
+  // max and one atomic.
+  uint32_t *const red = reinterpret_cast<uint32_t *>(smem + 2 * STB + kDynBytes);
+  int amax_pi = -1;
+  if constexpr (AMAX) {
+    if (lane == 0) red[wave] = 0;  // ordered before its first use by the first tile's barriers
+  }
+  auto flush_amax = [&]() {
+    if constexpr (AMAX) {
+      __syncthreads();  // every wave's last update of red is in
+      if (tid == 0 && amax_pi >= 0 && batch.p[amax_pi].amax_out) {
+        uint32_t m = red[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m = max(m, red[w]);
+        atomicMax(reinterpret_cast<uint32_t *>(batch.p[amax_pi].amax_out), m << 16);
+      }
+      __syncthreads();  // read before any wave clears its word
+      if (lane == 0) red[wave] = 0;
+    }
+  };
   uint32_t *const queue = DYN ? batch.queue + xcd * kQueueWords : nullptr;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void *)queue, (short)0, 4, 0x00020000);
   for (int it = local_wg; it < total;) {
@@ -196,6 +230,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         pi = i + 1;
       }
     int t = start[pi] + off;
+    if constexpr (AMAX) {
+      if (pi != amax_pi) {  // uniform: the workgroup moves on to another problem
+        if (amax_pi >= 0) flush_amax();
+        amax_pi = pi;
+      }
+    }
     const Problem P = batch.p[pi];
     const int M = P.M, N = P.N;
     const int ld = P.K;  // row stride of both operands
@@ -445,6 +485,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         (void *)(P.c + (int64_t)m0 * N), (short)0, (int)((uint32_t)rows_c * (uint32_t)N * 2u), 0x00020000);
     u32x4 vals[NCH];
     int offs[NCH];
+    uint32_t omag = 0;  // AMAX: this lane's max magnitude of the values it stores
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int idx = k * 64 + lane;
@@ -452,6 +493,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       vals[k] = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ (((row >> 2) & 1) << 6)));
       const int gcol = n0 + wn + ch * 8;
       offs[k] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
+      if constexpr (AMAX) {
+        // the values this chunk stores (padding rows may hold the bias: they do not count)
+        if (gcol < N && wm + row < rows_c)
+          omag = mag_max2(mag_max2(mag_max2(mag_max2(omag, vals[k].x), vals[k].y), vals[k].z), vals[k].w);
+      }
+    }
+    if constexpr (AMAX) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) omag = max(omag, (uint32_t)__shfl_xor((int)omag, off, 64));
+      if (lane == 0) red[wave] = max(red[wave], omag);
     }
     if (batch.nt_stores) {
 #pragma unroll
@@ -468,6 +519,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       it += wx;
     }
   }
+  if constexpr (AMAX) flush_amax();
   if constexpr (DYN) {
     // The last of the XCD's workgroups to get here clears its queue words.
     // Each workgroup's fetches have all returned (the last one ended its
@@ -536,6 +588,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const Problem P) {
   __syncthreads();
   if (wave == 0) {
     const float alpha = P.inv_a[0] * P.inv_b[0];
+    uint32_t omag = 0;  // max magnitude of the stored values (for amax_out)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const v4f_t t = red[0][m][lane] + red[1][m][lane] + red[2][m][lane] + red[3][m][lane];
@@ -543,8 +596,17 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const Problem P) {
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + 4 * (lane >> 4) + i, col = n0 + (lane & 15);
         const float bv = P.bias ? __uint_as_float((uint32_t)P.bias[col < N ? col : 0] << 16) : 0.0f;
-        if (row < M && col < N) P.c[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(t[i] * alpha + bv);
+        const uint32_t h = f32_to_bf16_rne(t[i] * alpha + bv);
+        if (row < M && col < N) {
+          P.c[(int64_t)row * N + col] = (uint16_t)h;
+          omag = max(omag, h & 0x7FFFu);
+        }
       }
+    }
+    if (P.amax_out) {  // one atomic max per workgroup
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) omag = max(omag, (uint32_t)__shfl_xor((int)omag, off, 64));
+      if (lane == 0) atomicMax(reinterpret_cast<uint32_t *>(P.amax_out), omag << 16);
     }
   }
 }
@@ -564,24 +626,49 @@ void launch_skinny(const Problem &p, hipStream_t stream) {
 
 // C = bf16(alpha * (sum over ranges of the fp32 partials, in range order)),
 // the same fp32 scaling and rounding as the tiled kernel's epilogue; four
-// elements per thread (M * N is a multiple of 16).
+// elements per thread per step of a grid-stride loop (M * N is a multiple of
+// 16).  amax_out (or null): max |C| folded in with one atomic per workgroup.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ part, int splits, int64_t mn,
                                                            const float *inv_a, const float *inv_b,
-                                                           uint16_t *__restrict__ c) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= mn) return;
-  float4 acc = *reinterpret_cast<const float4 *>(part + i);
-  for (int r = 1; r < splits; ++r) {
-    const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)r * mn + i);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
+                                                           uint16_t *__restrict__ c, float *amax_out) {
+  __shared__ uint32_t red[4];
   const float alpha = inv_a[0] * inv_b[0];
-  const bf16x2 lo = __builtin_convertvector(f32x2{acc.x * alpha, acc.y * alpha}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector(f32x2{acc.z * alpha, acc.w * alpha}, bf16x2);
-  *reinterpret_cast<u32x2 *>(c + i) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  uint32_t omag = 0;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 1024) {
+    float4 acc = *reinterpret_cast<const float4 *>(part + i);
+    for (int r = 1; r < splits; ++r) {
+      const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)r * mn + i);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const bf16x2 lo = __builtin_convertvector(f32x2{acc.x * alpha, acc.y * alpha}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector(f32x2{acc.z * alpha, acc.w * alpha}, bf16x2);
+    const uint32_t wlo = __builtin_bit_cast(uint32_t, lo), whi = __builtin_bit_cast(uint32_t, hi);
+    *reinterpret_cast<u32x2 *>(c + i) = u32x2{wlo, whi};
+    omag = mag_max2(mag_max2(omag, wlo), whi);
+  }
+  if (amax_out) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) omag = max(omag, (uint32_t)__shfl_xor((int)omag, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = omag;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      atomicMax(reinterpret_cast<uint32_t *>(amax_out), max(max(red[0], red[1]), max(red[2], red[3])) << 16);
+  }
+}
+
+// The tiled kernel with or without the output amax (only the forward's and
+// dgrad's format pairs produce a tensor a next layer casts).
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool DYN>
+void launch_tiled(const Batch &b, unsigned grid, bool amax, hipStream_t stream) {
+  constexpr bool kAmaxPair = FB == 0;
+  if (kAmaxPair && amax)
+    gemm_fp8_tn_kernel<FA, FB, BM, BN, WGM, WGN, MINB, G, false, DYN, kAmaxPair>
+        <<<grid, 64 * WGM * WGN, 0, stream>>>(b);
+  else
+    gemm_fp8_tn_kernel<FA, FB, BM, BN, WGM, WGN, MINB, G, false, DYN><<<grid, 64 * WGM * WGN, 0, stream>>>(b);
 }
 
 template <int FA, int FB>
@@ -604,6 +691,7 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       q.c = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(split_ws) + used);
       q.splits = s;
       q.bias = nullptr;
+      q.amax_out = nullptr;  // taken by the reduce kernel
       used += need;
     } else {
       rest.p[rest.count++] = p;
@@ -657,27 +745,28 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     // lines from the caches: stream it (measured: -3.5% time at 65536 x 4096 x
     // 4096, +2% at 4096^3 where each CU writes one tile).
     rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
+    bool amax = false;
+    for (int i = 0; i < rest.count; ++i) amax |= rest.p[i].amax_out != nullptr;
     if (use_big && mixed && queue) {
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;
-      gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, false, true>
-          <<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(rest);
+      launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_big) {
-      gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, false>
-          <<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(rest);
+      launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_med) {
-      gemm_fp8_tn_kernel<FA, FB, 64, 128, 2, 2, 2, 8, false>
-          <<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(rest);
+      launch_tiled<FA, FB, 64, 128, 2, 2, 2, 8, false>(rest, (unsigned)std::min(tiles, 2 * kCUs), amax, stream);
     } else {
-      gemm_fp8_tn_kernel<FA, FB, 128, 128, 2, 2, 2, 8, false>
-          <<<(unsigned)std::min(tiles, 2 * kCUs), 256, 0, stream>>>(rest);
+      launch_tiled<FA, FB, 128, 128, 2, 2, 2, 8, false>(rest, (unsigned)std::min(tiles, 2 * kCUs), amax, stream);
     }
   }
   for (int i = 0; i < split.count; ++i) {
     const Problem &q = split.p[i];
     const int64_t mn = (int64_t)q.M * q.N;
-    split_reduce_kernel<<<(unsigned)((mn / 4 + 255) / 256), 256, 0, stream>>>(
-        reinterpret_cast<const float *>(q.c), q.splits, mn, q.inv_a, q.inv_b, orig[i]->c);
+    // with an amax, at most one workgroup per CU (one atomic each)
+    const int64_t blocks = (mn / 4 + 255) / 256;
+    const unsigned grid = (unsigned)(orig[i]->amax_out ? std::min<int64_t>(blocks, kCUs) : blocks);
+    split_reduce_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<const float *>(q.c), q.splits, mn, q.inv_a,
+                                                  q.inv_b, orig[i]->c, orig[i]->amax_out);
   }
 }
 
@@ -713,6 +802,7 @@ hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipS
     p.inv_b = d[i].inv_b;
     p.c = d[i].c;
     p.bias = d[i].bias;
+    p.amax_out = d[i].amax_out;
     p.M = (int)d[i].M;
     p.N = (int)d[i].N;
     p.K = (int)d[i].K;

@@ -53,7 +53,16 @@ struct CastTensor {
   // colsum[tile_row * cols + col], for the bias gradient
   float *colsum = nullptr;
 };
-hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream);
+// Up to kMaxZero fp32 words the cast launch sets to +0 (from its first
+// workgroup) before anything later on the stream runs: the output-amax words
+// that the GEMM launch after it folds its results into.
+constexpr int kMaxZero = 4;
+struct ZeroWords {
+  float *w[kMaxZero] = {nullptr, nullptr, nullptr, nullptr};
+  int n = 0;
+};
+hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipStream_t stream,
+                       const ZeroWords &zero = ZeroWords());
 
 // Bias gradient: db[n] = bf16(sum over t < tiles of colsum[t * n_cols + n]),
 // summed in order of t.
@@ -74,6 +83,9 @@ struct GemmDesc {
   uint16_t *c;
   int64_t M, N, K;
   const uint16_t *bias = nullptr;  // (N) bf16 added to every row, or null
+  // if set: max |C| over the rounded bf16 output is folded into *amax_out
+  // (atomic max on the fp32 bit pattern; the word must hold +0 or less)
+  float *amax_out = nullptr;
 };
 // split_ws (optional, 16-byte aligned): room for the fp32 partial products of
 // problems split along K (split_factor > 1); a problem that does not fit

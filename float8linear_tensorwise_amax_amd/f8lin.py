@@ -54,7 +54,8 @@ class FwdArgs(ctypes.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("x", _vp), ("w", _vp), ("y", _vp),
                 ("x8", _vp), ("x8t", _vp), ("w8", _vp), ("w8t", _vp), ("sx", State), ("sw", State),
                 ("mode_x", _int), ("mode_w", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
-                ("bias", _vp), ("w_cast_valid", _int)]
+                ("bias", _vp), ("w_cast_valid", _int), ("ev_gemm_begin", _vp), ("ev_gemm_end", _vp),
+                ("y_amax", _vp), ("x_amax_given", _int)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -62,7 +63,8 @@ class BwdArgs(ctypes.Structure):
                 ("dx", _vp), ("dw", _vp), ("dy8", _vp), ("dy8t", _vp), ("sx", State), ("sw", State),
                 ("sdy", State), ("mode_dy", _int), ("algo", _int), ("ws", _vp), ("ws_bytes", ctypes.c_size_t),
                 ("dbias", _vp), ("dbias_ws", _vp), ("dbias_ws_bytes", ctypes.c_size_t), ("gemm_ws", _vp),
-                ("gemm_ws_bytes", ctypes.c_size_t)]
+                ("gemm_ws_bytes", ctypes.c_size_t), ("ev_gemm_begin", _vp), ("ev_gemm_end", _vp),
+                ("dx_amax", _vp), ("dy_amax_given", _int)]
 
 
 _lib.f8lin_workspace_bytes.argtypes = []
@@ -81,7 +83,7 @@ _lib.f8lin_gemm_batch.argtypes = [ctypes.POINTER(GemmDesc), _int, _int, _int, _v
 _lib.f8lin_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp]
 _lib.f8lin_forward_shared_x.argtypes = [ctypes.POINTER(FwdArgs), _int, _vp]
 _lib.f8lin_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp]
-_lib.f8lin_delayed_update.argtypes = [ctypes.POINTER(State), _int, _vp]
+_lib.f8lin_delayed_update.argtypes = [ctypes.POINTER(State), _int, _vp, _vp]
 for _name in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_cast_f32", "f8lin_gemm", "f8lin_forward",
               "f8lin_backward", "f8lin_delayed_update"):
     getattr(_lib, _name).restype = _int
@@ -157,7 +159,12 @@ class ScalingState:
     amax [1] f32, scale [2] f32 = {scale, 1/scale}, history [16] f32,
     hist_meta [2] i32 = {count, pos}; all zero-initialised."""
 
-    def __init__(self, device="cuda"):
+    def __init__(self, device="cuda", tensors=None):
+        """tensors: optional (amax, scale, history, hist_meta) tensors to wrap
+        instead of allocating new ones (e.g. a module's buffers)."""
+        if tensors is not None:
+            self.amax, self.scale, self.history, self.hist_meta = tensors
+            return
         self.amax = torch.zeros(1, dtype=torch.float32, device=device)
         self.scale = torch.zeros(2, dtype=torch.float32, device=device)
         self.history = torch.zeros(HISTORY_LEN, dtype=torch.float32, device=device)
@@ -240,43 +247,73 @@ def gemm_batch(items, fmt_a, fmt_b, stream=None):
     _check(_lib.f8lin_gemm_batch(arr, len(items), _FMT[fmt_a], _FMT[fmt_b], _stream(stream)))
 
 
-def _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias, w_cast_valid):
+def _event(ev) -> Optional[int]:
+    """Raw hipEvent_t of a torch.cuda.Event (created by recording it once), or None."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return ev.cuda_event
+
+
+def _amax_word(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() < 1:
+        raise TypeError("f8lin: an amax output is a float32 tensor")
+    return _ptr(t)
+
+
+def _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias, w_cast_valid, gemm_events=None,
+              y_amax=None, x_amax_given=False):
     M, K = x.shape
     N = w8.shape[0]
     if (w is not None and tuple(w.shape) != (N, K)) or tuple(w8.shape) != (N, K) or tuple(y.shape) != (M, N):
         raise ValueError("forward: shape mismatch")
     if bias is not None and tuple(bias.shape) != (N,):
         raise ValueError("forward: bias must have shape (N,)")
+    ev0, ev1 = (None, None) if gemm_events is None else gemm_events
     return FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
                    _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
                    sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
                    _nbytes(ws), None if bias is None else _ptr(bias, torch.bfloat16),
-                   1 if w_cast_valid else 0)
+                   1 if w_cast_valid else 0, _event(ev0), _event(ev1), _amax_word(y_amax),
+                   1 if x_amax_given else 0)
 
 
 def forward(x, w, y, x8, x8t, w8, w8t, sx: ScalingState, sw: ScalingState, ws, mode_x="dynamic",
-            mode_w="dynamic", algo="atomic", stream=None, bias=None, w_cast_valid=False):
+            mode_w="dynamic", algo="atomic", stream=None, bias=None, w_cast_valid=False, gemm_events=None,
+            y_amax=None, x_amax_given=False):
     """w_cast_valid: w8, w8t and sw's scale already hold W's cast (unchanged
-    weight); W's amax and cast are skipped and w may be None."""
-    a = _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias, w_cast_valid)
+    weight); W's amax and cast are skipped and w may be None.
+    gemm_events: optional (begin, end) torch.cuda.Event pair recorded around
+    the call's GEMM launch.  y_amax: optional float32 tensor that receives
+    amax(Y) from the GEMM epilogue.  x_amax_given: sx.amax already holds
+    amax(X) (dynamic mode), so X's amax pass is skipped."""
+    a = _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias, w_cast_valid, gemm_events,
+                  y_amax, x_amax_given)
     _check(_lib.f8lin_forward(ctypes.byref(a), _stream(stream)))
 
 
-def forward_shared_x(x, x8, x8t, sx: ScalingState, ws, linears, mode_x="dynamic", algo="atomic", stream=None):
+def forward_shared_x(x, x8, x8t, sx: ScalingState, ws, linears, mode_x="dynamic", algo="atomic", stream=None,
+                     gemm_events=None, x_amax_given=False):
     """Linears reading the same X: linears is a list of dicts with keys w, y,
-    w8, w8t, sw and optionally mode_w, bias, w_cast_valid.  X is cast once;
-    the GEMMs share one launch."""
+    w8, w8t, sw and optionally mode_w, bias, w_cast_valid, y_amax.  X is cast
+    once; the GEMMs share one launch."""
     arr = (FwdArgs * max(1, len(linears)))()
     for i, l in enumerate(linears):
         arr[i] = _fwd_args(x, l.get("w"), l["y"], x8, x8t, l["w8"], l["w8t"], sx, l["sw"], ws, mode_x,
-                           l.get("mode_w", "dynamic"), algo, l.get("bias"), l.get("w_cast_valid", False))
+                           l.get("mode_w", "dynamic"), algo, l.get("bias"), l.get("w_cast_valid", False),
+                           gemm_events, l.get("y_amax"), x_amax_given)
     _check(_lib.f8lin_forward_shared_x(arr, len(linears), _stream(stream)))
 
 
 def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState, sdy: ScalingState, ws,
-             mode_dy="dynamic", algo="atomic", stream=None, dbias=None, dbias_ws=None, gemm_ws=None):
+             mode_dy="dynamic", algo="atomic", stream=None, dbias=None, dbias_ws=None, gemm_ws=None,
+             gemm_events=None, dx_amax=None, dy_amax_given=False):
     """gemm_ws: optional scratch (backward_gemm_workspace_bytes(M, N, K) bytes) with which GEMMs that have
-    few output tiles and a long contraction run split along K."""
+    few output tiles and a long contraction run split along K.  gemm_events, dx_amax, dy_amax_given: as
+    forward's gemm_events, y_amax, x_amax_given, for the dgrad + wgrad launch, dX and dY."""
     M, N = dy.shape
     K = x8t.shape[0]
     if tuple(dx.shape) != (M, K) or tuple(dw.shape) != (N, K) or tuple(w8t.shape) != (K, N):
@@ -288,13 +325,20 @@ def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState
                 sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], _ptr(ws),
                 _nbytes(ws), None if dbias is None else _ptr(dbias, torch.bfloat16),
                 None if dbias_ws is None else _ptr(dbias_ws, torch.float32),
-                0 if dbias_ws is None else dbias_ws.numel() * 4, _ptr(gemm_ws), _nbytes(gemm_ws))
+                0 if dbias_ws is None else dbias_ws.numel() * 4, _ptr(gemm_ws), _nbytes(gemm_ws),
+                *((None, None) if gemm_events is None else (_event(gemm_events[0]), _event(gemm_events[1]))),
+                _amax_word(dx_amax), 1 if dy_amax_given else 0)
     _check(_lib.f8lin_backward(ctypes.byref(a), _stream(stream)))
 
 
-def delayed_update(states: Sequence[ScalingState], stream=None):
+def delayed_update(states: Sequence[ScalingState], stream=None, status: Optional[torch.Tensor] = None):
+    """status: optional int32 device tensor of len(states); entry i becomes 0
+    when state i was updated and 1 (F8LIN_EINVAL) when its {count, pos} was
+    not a reachable one, in which case that state is left untouched."""
     arr = (State * max(1, len(states)))(*[s.c_struct() for s in states])
-    _check(_lib.f8lin_delayed_update(arr, len(states), _stream(stream)))
+    if status is not None and (status.dtype != torch.int32 or status.numel() < len(states)):
+        raise ValueError("delayed_update: status must be an int32 tensor of at least len(states) entries")
+    _check(_lib.f8lin_delayed_update(arr, len(states), _ptr(status), _stream(stream)))
 
 
 # ------------------------------------------------------------ layer buffers
@@ -324,14 +368,14 @@ class LinearBuffers:
         self.dbias_ws = new_dbias_workspace(M, N, device) if with_bias else None
         self.gemm_ws = new_backward_gemm_workspace(M, N, K, device)
 
-    def forward(self, x, w, mode="dynamic", algo="atomic", stream=None, bias=None):
+    def forward(self, x, w, mode="dynamic", algo="atomic", stream=None, bias=None, gemm_events=None):
         forward(x, w, self.y, self.x8, self.x8t, self.w8, self.w8t, self.sx, self.sw, self.ws, mode, mode, algo,
-                stream, bias)
+                stream, bias, gemm_events=gemm_events)
         return self.y
 
-    def backward(self, dy, mode="dynamic", algo="atomic", stream=None):
+    def backward(self, dy, mode="dynamic", algo="atomic", stream=None, gemm_events=None):
         backward(dy, self.x8t, self.w8t, self.dx, self.dw, self.dy8, self.dy8t, self.sx, self.sw, self.sdy,
-                 self.ws, mode, algo, stream, self.dbias, self.dbias_ws, self.gemm_ws)
+                 self.ws, mode, algo, stream, self.dbias, self.dbias_ws, self.gemm_ws, gemm_events=gemm_events)
         return self.dx, self.dw
 
     def states(self):

@@ -102,8 +102,11 @@ typedef struct {
 } f8lin_state;
 
 /* Bytes of device workspace that f8lin_amax / f8lin_forward /
- * f8lin_backward need (a constant).  The caller zero-fills it once before
- * first use.  Every call leaves the words that must start at zero (the
+ * f8lin_backward need.  A constant: the amax grid is capped at one
+ * workgroup per compute unit, so no tensor size needs more (the scratch of
+ * both amax algorithms of pytorch/torchtitan PR #778's single-linear-layer
+ * table, ATOMIC_MAX and REDUCTION, plus the backward GEMM's work queue).
+ * The caller zero-fills it once before first use.  Every call leaves the words that must start at zero (the
  * atomic algorithm's running maxima and tickets, the backward GEMM's
  * work-queue counters) at zero again; f8lin_amax
  * leaves the whole workspace zero-filled, while f8lin_forward /
@@ -111,27 +114,48 @@ typedef struct {
  * the workspace (every call overwrites them before reading them). */
 size_t f8lin_workspace_bytes(void);
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string, never NULL; an
+ * unknown code gives "unknown f8lin status"). */
 const char *f8lin_status_str(int status);
 
-/* amax of a bf16 tensor of n elements -> amax_out[0] (fp32).  The result is
- * exact (it is one of the inputs' magnitudes), the same for both algorithms
- * and for every launch order; NaN inputs make it NaN; n = 0 gives 0.
- * algo: f8lin_amax_algo.  ws: workspace of >= f8lin_workspace_bytes(). */
+/* amax of a bf16 tensor of n elements -> amax_out[0] (fp32): the tensorwise
+ * absolute maximum that dynamic scaling takes its scale from
+ * (pytorch/torchtitan PR #778, Summary, and its single-linear-layer table's
+ * kernel_algo column: ATOMIC_MAX = F8LIN_AMAX_ATOMIC, REDUCTION =
+ * F8LIN_AMAX_TWOPASS).  The result is exact (it is one of the inputs'
+ * magnitudes), the same for both algorithms and for every launch order; NaN
+ * inputs make it NaN; n = 0 gives 0.  x: n bf16 values, 16-byte aligned.
+ * algo: f8lin_amax_algo.  ws: workspace of >= f8lin_workspace_bytes().
+ * Errors: EINVAL (null amax_out, bad algo, output overlapping x), ESHAPE
+ * (n < 0 or above 2^40), EALIGN, EWORKSPACE. */
 int f8lin_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, void *ws, size_t ws_bytes,
                void *stream);
 
 /* Scale and cast of a bf16 (rows, cols) tensor to fp8 codes q (rows, cols),
- * and, if qt != NULL, the transposed copy qt (cols, rows), in one pass.
+ * and, if qt != NULL, the transposed copy qt (cols, rows), in one pass: the
+ * "fp8 conversion" step that float8nocompile writes as handwritten kernels
+ * (pytorch/torchtitan PR #778, Summary), with the scale taken as in
+ * tensorwise dynamic or delayed scaling (pytorch/ao issue #1297, repro
+ * script, CastConfig(ScalingType.DELAYED)).  The transposed copy is the
+ * operand layout the backward GEMMs contract over.
  * fmt: f8lin_fmt.  mode: f8lin_scaling (see above).  The scale and inverse
- * scale the cast used are stored to st->scale[0..1]. */
+ * scale the cast used are stored to st->scale[0..1]; in delayed mode this
+ * tensor's amax is also folded into st->amax.
+ * Errors: EINVAL (null state or state fields, bad enum, outputs overlapping
+ * inputs), ESHAPE, EALIGN; nothing is launched on error. */
 int f8lin_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
                          const f8lin_state *st, uint8_t *q, uint8_t *qt, void *stream);
 
-/* The conversion alone, on fp32 values (scale 1): q[i] = RNE_sat(v[i]). */
+/* The conversion alone, on fp32 values (scale 1): q[i] = RNE_sat(v[i]), the
+ * rounding step of the cast above (for checking the conversion on every
+ * binary32 input).  v: n fp32 values; q: n codes; both 16-byte aligned.
+ * Errors: EINVAL, ESHAPE, EALIGN. */
 int f8lin_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, void *stream);
 
-/* fp8 GEMM with a per-tensor dequantisation epilogue:
+/* fp8 GEMM with a per-tensor dequantisation epilogue, the product every
+ * GEMM of the layer's forward + backward is an instance of (pytorch/torchtitan
+ * PR #778, "Benchmarking single linear layer forward+backward
+ * performance"):
  *   C (M, N) bf16 = (A (M, K) . B (N, K)^T) * inv_scale_a[0] * inv_scale_b[0]
  * A and B are fp8 codes in formats fmt_a / fmt_b, both contiguous along K;
  * products are exact and accumulate in fp32; the result is rounded once to
@@ -157,7 +181,9 @@ typedef struct {
 } f8lin_gemm_desc;
 int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, void *stream);
 
-/* Forward of the layer: X (M, K) bf16, W (N, K) bf16 -> Y (M, N) bf16.
+/* Forward of the layer (pytorch/torchtitan PR #778, "Benchmarking single
+ * linear layer forward+backward performance", the forward half):
+ * X (M, K) bf16, W (N, K) bf16 -> Y (M, N) bf16.
  * Per tensor: amax (dynamic mode only), then one cast writing both layouts;
  * then Y = X8 . W8^T with the dequantisation epilogue.  x8t and w8t (and the
  * scales in sx, sw) are what backward needs; x8 and w8 can be reused or
@@ -182,9 +208,25 @@ typedef struct {
    * of one optimizer step), so W's amax and cast are skipped and w is not
    * read. */
   int w_cast_valid;
+  /* Optional (NULL = none) hipEvent_t handles, recorded on `stream` right
+   * before and right after the call's GEMM launch: the duration of the
+   * GEMM the call itself issues, for profiling. */
+  void *ev_gemm_begin, *ev_gemm_end;
+  /* Optional (NULL = none), 4-byte aligned: receives max |Y| over the bf16
+   * values of Y (the amax of Y, exact, as f8lin_amax would give it), taken
+   * in the GEMM's epilogue.  Handing it to the next layer as its sx.amax
+   * with x_amax_given spares that layer its amax pass over Y: the float8
+   * ops fused with the op that produces their input (pytorch/ao issue
+   * #1199, the reply on the ops not being fused with surrounding ops). */
+  float *y_amax;
+  /* Nonzero (dynamic mode only): sx.amax already holds amax(X) -- e.g. the
+   * y_amax of the layer that produced X -- so X's amax pass is skipped. */
+  int x_amax_given;
 } f8lin_fwd_args;
 
-/* Backward of the layer, given dY (M, N) bf16 and the forward's saved x8t,
+/* Backward of the layer (pytorch/torchtitan PR #778, "Benchmarking single
+ * linear layer forward+backward performance", the backward half), given
+ * dY (M, N) bf16 and the forward's saved x8t,
  * w8t and scaling states: dY is cast once to e5m2 (both layouts), then
  * dX (M, K) = dY8 . W8 (contraction over N, B operand w8t) and
  * dW (N, K) = dY8^T . X8 (contraction over M, A operand dy8t, B operand x8t),
@@ -225,38 +267,70 @@ typedef struct {
   size_t dbias_ws_bytes;
   void *gemm_ws;                /* scratch for split GEMMs, or NULL */
   size_t gemm_ws_bytes;
+  void *ev_gemm_begin, *ev_gemm_end; /* as in f8lin_fwd_args (around the dgrad + wgrad launch) */
+  float *dx_amax;               /* optional: receives amax(dX), as y_amax does amax(Y) */
+  int dy_amax_given;            /* nonzero (dynamic mode only): sdy.amax holds amax(dY) */
 } f8lin_bwd_args;
 
-/* Bytes of dbias_ws that f8lin_backward needs for an (M, N) dY:
- * max(1, ceil(M / 128)) * N * 4. */
+/* Bytes of dbias_ws that f8lin_backward needs for an (M, N) dY, for the
+ * gradient of the bias the repro's nn.Linear layers keep (pytorch/ao issue
+ * #1297, repro script): max(1, ceil(M / 128)) * N * 4.  0 for M or N < 0. */
 size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N);
 
 /* Bytes of gemm_ws with which f8lin_backward splits every GEMM of an
- * (M, N, K) layer that it would split (0: none is split at this shape; also
- * 0 for invalid dimensions).  With less, GEMMs whose partials do not fit run
- * unsplit. */
+ * (M, N, K) layer that it would split (the backward GEMMs of pytorch/
+ * torchtitan PR #778's single-linear-layer benchmark; 0: none is split at
+ * this shape; also 0 for invalid dimensions).  With less, GEMMs whose
+ * partials do not fit run unsplit. */
 size_t f8lin_backward_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* The forward described above f8lin_fwd_args.  Errors, all checked before
+ * anything is launched: EINVAL (null args or required pointers, bad enums,
+ * a delayed state without history, x_amax_given outside dynamic mode,
+ * any output overlapping another output or an input), ESHAPE, EALIGN,
+ * EWORKSPACE (a dynamic-mode amax pass without a valid workspace); EHIP if
+ * a launch fails. */
 int f8lin_forward(const f8lin_fwd_args *args, void *stream);
 
 /* Forward of count (1 .. F8LIN_MAX_BATCH) linears that read the same input X,
  * such as the q, k and v projections of an attention block or the two input
- * projections of a gated MLP: X is cast once (amax, scale, X8, X8^T), each
+ * projections of a gated MLP (the Llama3 8b layer of pytorch/torchtitan
+ * PR #778's training table has both): X is cast once (amax, scale, X8, X8^T), each
  * weight as in f8lin_forward, and the count GEMMs run in one launch.  Every
  * entry gives the same M, K, x, x8, x8t, sx, mode_x, algo and workspace;
- * N, w, y, w8, w8t, sw, mode_w, bias and w_cast_valid are per entry.  Each
+ * N, w, y, w8, w8t, sw, mode_w, bias, w_cast_valid and y_amax are per
+ * entry, and ev_gemm_begin / ev_gemm_end and x_amax_given are shared.  Each
  * output equals, bit for bit, what f8lin_forward gives for that entry.
  * Errors: as f8lin_forward for each entry; entries that disagree on the
  * shared fields, or outputs that overlap any entry's input or output, are
  * F8LIN_EINVAL; nothing is launched unless every entry is valid. */
 int f8lin_forward_shared_x(const f8lin_fwd_args *args, int count, void *stream);
+
+/* The backward described above f8lin_bwd_args.  Errors, all checked before
+ * anything is launched: EINVAL (null args or required pointers, bad enums,
+ * dy_amax_given outside dynamic mode, overlapping buffers -- the split
+ * scratch counts for the part that split GEMMs would use), ESHAPE, EALIGN,
+ * EWORKSPACE (dynamic mode without a valid workspace, a bias gradient
+ * without enough dbias_ws); EHIP if a launch fails. */
 int f8lin_backward(const f8lin_bwd_args *args, void *stream);
 
-/* After backward (the sync step of delayed scaling), for each of the
- * n_states states: history[pos] = amax; pos = (pos + 1) % 16;
- * count = min(count + 1, 16); amax = 0.  Every state needs history and
- * hist_meta. */
-int f8lin_delayed_update(const f8lin_state *states, int n_states, void *stream);
+/* After backward, the sync step of delayed scaling
+ * (pytorch/ao issue #1297, repro script: sync_float8_amax_and_scale_history
+ * after loss.backward()), for each of the n_states states:
+ *   history[pos] = amax; pos = (pos + 1) % 16; count = min(count + 1, 16);
+ *   amax = 0.
+ * Every state needs amax, history (16-byte aligned) and hist_meta.
+ * A state's {count, pos} must be one those pushes reach from the zeroed
+ * state: 0 <= count <= 16, 0 <= pos <= 15, and pos == count while
+ * count < 16.  The host cannot see device memory, so this is checked on the
+ * device: a state that fails it (e.g. restored from a corrupted checkpoint)
+ * is left untouched -- history, meta and amax -- and, if status is not
+ * NULL, status[i] (a device int32 array of n_states, 4-byte aligned) is set
+ * to F8LIN_EINVAL for it and to F8LIN_OK for every state updated.
+ * Errors (host-side, before any launch): EINVAL (null states, a state
+ * without amax / history / hist_meta, n_states < 0, status overlapping a
+ * state), EALIGN. */
+int f8lin_delayed_update(const f8lin_state *states, int n_states, int32_t *status, void *stream);
 
 #ifdef __cplusplus
 }

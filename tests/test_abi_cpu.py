@@ -158,7 +158,8 @@ class Fwd(ctypes.Structure):
                [(n, ctypes.c_void_p) for n in ("x", "w", "y", "x8", "x8t", "w8", "w8t")] + \
                [("sx", State), ("sw", State), ("mode_x", ctypes.c_int), ("mode_w", ctypes.c_int),
                 ("algo", ctypes.c_int), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
-                ("bias", ctypes.c_void_p), ("w_cast_valid", ctypes.c_int)]
+                ("bias", ctypes.c_void_p), ("w_cast_valid", ctypes.c_int), ("ev_gemm_begin", ctypes.c_void_p),
+                ("ev_gemm_end", ctypes.c_void_p), ("y_amax", ctypes.c_void_p), ("x_amax_given", ctypes.c_int)]
 
 
 class Bwd(ctypes.Structure):
@@ -167,7 +168,8 @@ class Bwd(ctypes.Structure):
                [("sx", State), ("sw", State), ("sdy", State), ("mode_dy", ctypes.c_int), ("algo", ctypes.c_int),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("dbias", ctypes.c_void_p),
                 ("dbias_ws", ctypes.c_void_p), ("dbias_ws_bytes", ctypes.c_size_t), ("gemm_ws", ctypes.c_void_p),
-                ("gemm_ws_bytes", ctypes.c_size_t)]
+                ("gemm_ws_bytes", ctypes.c_size_t), ("ev_gemm_begin", ctypes.c_void_p), ("ev_gemm_end", ctypes.c_void_p),
+                ("dx_amax", ctypes.c_void_p), ("dy_amax_given", ctypes.c_int)]
 
 
 def test_backward_rejections(lib):
@@ -198,6 +200,13 @@ def test_backward_rejections(lib):
     assert f(ctypes.byref(args(dbias=DB + 2, dbias_ws=DBWS, dbias_ws_bytes=need)), None) == EALIGN
     assert f(ctypes.byref(args(dbias=DB, dbias_ws=A, dbias_ws_bytes=need)), None) == EINVAL  # scratch is dY
     assert f(ctypes.byref(args(dbias=A + MB, dbias_ws=DBWS, dbias_ws_bytes=need)), None) == EINVAL  # dbias in x8t
+    # amax of dX from the epilogue: a 4-byte aligned word outside every other buffer
+    assert f(ctypes.byref(args(dx_amax=AMAX + 256 + 2)), None) == EALIGN
+    assert f(ctypes.byref(args(dx_amax=A + 3 * MB + 64)), None) == EINVAL                  # inside dX
+    assert f(ctypes.byref(args(dx_amax=SCALE + 128)), None) == EINVAL                       # dY's scale
+    # dY's amax handed in: dynamic mode only
+    assert f(ctypes.byref(args(dy_amax_given=1, mode_dy=1, sdy=State(AMAX + 128, SCALE + 128, HIST, META))),
+             None) == EINVAL
 
 
 def test_backward_gemm_workspace(lib):
@@ -264,6 +273,13 @@ def test_forward_rejections(lib):
     # a reused weight cast: w is not read (null allowed), but w8 / w8t / scale must be there
     assert f(ctypes.byref(args(w_cast_valid=1, w=None, sw=State(AMAX + 64, None, None, None))), None) == EINVAL
     assert f(ctypes.byref(args(w_cast_valid=1, w=None, w8=None)), None) == EINVAL
+    # amax of Y from the epilogue, and X's amax handed in
+    assert f(ctypes.byref(args(y_amax=AMAX + 256 + 1)), None) == EALIGN
+    assert f(ctypes.byref(args(y_amax=A + 2 * MB + 32)), None) == EINVAL                    # inside Y
+    assert f(ctypes.byref(args(y_amax=AMAX)), None) == EINVAL                               # X's own amax word
+    assert f(ctypes.byref(args(x_amax_given=1, mode_x=1, sx=State(AMAX, SCALE, HIST, META))), None) == EINVAL
+    # X's amax is read, not written, when handed in: still no output may cover it
+    assert f(ctypes.byref(args(x_amax_given=1, y_amax=AMAX)), None) == EINVAL
     # shared X: every entry must agree on X and its state
     g = lib.f8lin_forward_shared_x
     g.argtypes = [ctypes.POINTER(Fwd), ctypes.c_int, ctypes.c_void_p]
@@ -282,10 +298,15 @@ def test_forward_rejections(lib):
 
 def test_delayed_update_rejections(lib):
     f = lib.f8lin_delayed_update
-    f.argtypes = [ctypes.POINTER(State), ctypes.c_int, ctypes.c_void_p]
+    f.argtypes = [ctypes.POINTER(State), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     f.restype = ctypes.c_int
     arr = (State * 2)(State(AMAX, SCALE, HIST, META), State(AMAX, SCALE, None, META))
-    assert f(arr, 2, None) == EINVAL
-    assert f(arr, -1, None) == EINVAL
+    assert f(arr, 2, None, None) == EINVAL
+    assert f(arr, -1, None, None) == EINVAL
+    assert f(None, 1, None, None) == EINVAL
     arr2 = (State * 1)(State(AMAX, SCALE, HIST + 4, META))
-    assert f(arr2, 1, None) == EALIGN
+    assert f(arr2, 1, None, None) == EALIGN
+    ok = (State * 1)(State(AMAX, SCALE, HIST, META))
+    assert f(ok, 1, C + 2, None) == EALIGN         # status words are int32
+    assert f(ok, 1, HIST + 8, None) == EINVAL      # status inside the history
+    assert f(ok, 1, META + 4, None) == EINVAL      # status inside {count, pos}
