@@ -21,7 +21,7 @@ from .reference import (  # noqa: F401
     E4M3, E5M2, FMAX, HIST_LEN, EPS,
     amax, scale, cast, encode_f32, encode_bits_range, decode, decode_table,
     bf16_bits_to_f32, fp8_encode_scalar, fp8_decode_scalar,
-    forward_ref, dgrad_ref, wgrad_ref, forward_ref_at, dgrad_ref_at, wgrad_ref_at,
+    gemm_ref, forward_ref, dgrad_ref, wgrad_ref, forward_ref_at, dgrad_ref_at, wgrad_ref_at,
     bf16_to_f64, dbias_ref,
     DelayedHistory, linear_step, lib_path,
 )

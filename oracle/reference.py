@@ -166,6 +166,15 @@ def encode_bits_range(lo: int, count: int, fmt: int) -> np.ndarray:
 # decodes exactly to fp64, each product of two fp8 values is exact in fp64,
 # the sums are fp64, and the result is divided by both tensor scales.
 
+def gemm_ref(a8, fmt_a, b8, fmt_b, sa, sb):
+    """C (M, N) = (A8 . B8^T) / (s_a s_b) for fp8 codes A8 (M, K) in format
+    fmt_a and B8 (N, K) in fmt_b, both laid out along K (the one product all
+    three GEMMs of the layer are instances of, given the transposed copies)."""
+    a = decode(a8, fmt_a)
+    b = decode(b8, fmt_b)
+    return (a @ b.T) / np.float64(sa) / np.float64(sb)
+
+
 def forward_ref(x8, w8, sx, sw, bias_bits=None):
     """Y (M, N) = (X8 . W8^T) / (s_x s_w) [+ b], X8 (M, K) e4m3, W8 (N, K) e4m3,
     b (N,) bf16 bits added to every row."""

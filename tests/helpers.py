@@ -1,5 +1,5 @@
-"""Shared helpers for the parity tests: conversions, the GEMM tolerance and
-sampled references.
+"""Shared helpers for the parity tests: conversions and the GEMM tolerance,
+checked on whole outputs.
 
 GEMM tolerance (per element): |gpu - ref| <= 1e-2 * rms(ref) + ulp_bf16(|ref|),
 with ulp_bf16(y) = 2^(floor(log2 y) - 7) for y >= 2^-126 and 2^-133 below;
@@ -33,9 +33,11 @@ def np_f32_bits(x) -> np.uint32:
 
 
 def bf16_ulp(y: np.ndarray) -> np.ndarray:
+    """2^(floor(log2 |y|) - 7) for |y| >= 2^-126, else 2^-133.  frexp gives
+    |y| = m 2^e with m in [0.5, 1), so floor(log2 |y|) = e - 1 exactly."""
     a = np.abs(y)
-    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
-    return np.where(a >= 2.0 ** -126, 2.0 ** (e - 7), 2.0 ** -133)
+    _, e = np.frexp(np.maximum(a, 2.0 ** -126))
+    return np.where(a >= 2.0 ** -126, np.ldexp(1.0, e - 8), 2.0 ** -133)
 
 
 def gemm_check(got: np.ndarray, ref: np.ndarray, rms: float = None, what: str = ""):
@@ -52,26 +54,20 @@ def gemm_check(got: np.ndarray, ref: np.ndarray, rms: float = None, what: str = 
     return float(err.max() / max(rms, 1e-300)) if err.size else 0.0
 
 
-def sample_rows(n: int, k: int, seed: int) -> np.ndarray:
-    """k distinct row indices in [0, n) that always include the first and the
-    last 16 (the edge tiles) plus a seeded random spread."""
-    if n <= k:
-        return np.arange(n)
-    rng = np.random.default_rng(seed)
-    edge = np.concatenate([np.arange(min(16, n)), np.arange(max(0, n - 16), n)])
-    rest = rng.choice(n, size=k, replace=False)
-    return np.unique(np.concatenate([edge, rest]))
+def rms_of(ref: np.ndarray) -> float:
+    """Root mean square of a whole fp64 array (one BLAS dot, no temporary)."""
+    flat = ref.reshape(-1)
+    return float(np.sqrt(np.dot(flat, flat) / flat.size)) if flat.size else 0.0
 
 
-def forward_rows(x8, w8, sx, sw, rows):
-    """Rows `rows` of the oracle's Y (same definition, on a row subset)."""
-    return oracle.forward_ref(x8[rows], w8, sx, sw)
-
-
-def dgrad_rows(dy8, w8, sdy, sw, rows):
-    return oracle.dgrad_ref(dy8[rows], w8, sdy, sw)
-
-
-def wgrad_rows(dy8, x8, sdy, sx, rows):
-    """Rows `rows` of the oracle's dW = dY8^T X8 (rows index N)."""
-    return oracle.wgrad_ref(np.ascontiguousarray(dy8[:, rows]), x8, sdy, sx)
+def gemm_check_dev(got_dev: torch.Tensor, ref: np.ndarray, what: str = "", chunk_rows: int = 4096) -> float:
+    """gemm_check of a whole device output against the whole fp64 reference,
+    copied to the host and compared in blocks of rows (every element is
+    checked; rms is taken over the whole reference)."""
+    assert tuple(got_dev.shape) == ref.shape, (what, tuple(got_dev.shape), ref.shape)
+    rms = rms_of(ref)
+    worst = 0.0
+    for r0 in range(0, ref.shape[0], chunk_rows):
+        r1 = min(ref.shape[0], r0 + chunk_rows)
+        worst = max(worst, gemm_check(bf16_to_f64(got_dev[r0:r1]), ref[r0:r1], rms=rms, what=f"{what} rows {r0}:{r1}"))
+    return worst

@@ -406,6 +406,30 @@ def test_gemm_refs_against_exact_rational_arithmetic():
                 assert abs(Fraction(float(got[i, j])) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
 
 
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
+def test_gemm_ref_any_formats_against_exact_rational_arithmetic(fa, fb):
+    """The format-generic reference C = A8 B8^T / (s_a s_b): every operand
+    code over its whole finite range (both signs), each format decoded as
+    its own, against the Fraction triple loop; distinct M, N, K so that a
+    transposed or swapped operand cannot fit."""
+    rng = np.random.default_rng(31 + 2 * fa + fb)
+    M, N, K = 4, 6, 11
+    a8 = _codes(rng, (M, K), fa)
+    b8 = _codes(rng, (N, K), fb)
+    sa, sb = np.float32(0.1875), np.float32(640.0)
+    exact = _exact_matmul(_frac(a8, fa), _frac(b8, fb), transpose_b=True)
+    den = Fraction(float(sa)) * Fraction(float(sb))
+    got = oracle.gemm_ref(a8, fa, b8, fb, sa, sb)
+    assert got.shape == (M, N)
+    for i in range(M):
+        for j in range(N):
+            want = exact[i][j] / den
+            assert abs(Fraction(float(got[i, j])) - want) <= abs(want) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+    # decoding with the other format changes the result: the formats are not mixed up
+    if fa != fb:
+        assert not np.array_equal(got, oracle.gemm_ref(a8, fb, b8, fa, sa, sb))
+
+
 def test_bias_refs_against_exact_rational_arithmetic():
     """Y = X8 W8^T / (s_x s_w) + b and db = column sums of dY, against
     Fractions written from the definitions."""
