@@ -15,6 +15,26 @@ exact (zero rows raise no amax, add nothing to dW or to the bias gradient,
 and their Y / dX rows are dropped).  A bias (the repro's nn.Linear layers
 keep theirs) is added in the GEMM epilogue and its gradient is summed in the
 backward's cast pass.
+
+Scaling state.  Each layer keeps, per tensor role (input x, weight w,
+grad_output dy), the device state the library reads and writes -- amax,
+{scale, 1/scale}, the 16-entry amax history and {count, pos} -- as
+registered buffers, so model.state_dict() / load_state_dict() save and
+restore it and model.to() moves it; which delayed roles have taken their
+first step is saved as the module's extra state.
+
+Delayed scaling, per role:
+  * the scale comes from the largest amax of the previous steps (the
+    history), and the cast folds this step's amax into the state;
+  * a role's first step has no history: it takes its scale from the current
+    tensor (amax initialisation).  It runs through the same delayed cast with
+    a one-entry history seeded with the current tensor's amax (computed by
+    the library's amax pass), so the scale is the dynamic one, bit for bit,
+    and the state's amax still collects the maximum over every micro-batch
+    of the step;
+  * the sync after backward pushes the amax of every delayed role that has
+    produced one since the last sync (a forward without backward produces
+    none for dy), and only those roles count as initialised.
 """
 from dataclasses import dataclass, field
 from typing import Dict, Optional
@@ -23,6 +43,10 @@ import torch
 import torch.nn as nn
 
 from . import f8lin
+
+_ROLES = ("x", "w", "dy")
+_STATE_FIELDS = (("amax", (1,), torch.float32), ("scale", (2,), torch.float32),
+                 ("history", (f8lin.HISTORY_LEN,), torch.float32), ("hist_meta", (2,), torch.int32))
 
 
 @dataclass
@@ -40,9 +64,13 @@ class Float8LinearConfig:
     cast_config_weight: CastConfig = field(default_factory=CastConfig)
     cast_config_grad_output: CastConfig = field(default_factory=CastConfig)
     amax_algo: str = "twopass"  # "atomic" or "twopass"
-    # Reuse the weight's fp8 copies while the weight is unchanged (same tensor,
-    # same version counter: e.g. the micro-batches of one optimizer step).
-    reuse_weight_cast: bool = True
+    # Opt-in: reuse the weight's fp8 copies while the weight tensor and its
+    # version counter are unchanged (e.g. the micro-batches of one optimizer
+    # step).  Updates through .data (p.data.copy_, EMA, checkpoint loading)
+    # do not move the version counter: after such an update call
+    # invalidate_weight_cast(model).  The cache is also dropped at every
+    # sync_float8_amax_and_scale_history.
+    reuse_weight_cast: bool = False
 
 
 def _pad_rows(t: torch.Tensor) -> torch.Tensor:
@@ -58,35 +86,36 @@ class _Float8LinearFn(torch.autograd.Function):
     def forward(ctx, x2d, weight, bias, layer):
         M0 = x2d.shape[0]
         x = _pad_rows(x2d.to(torch.bfloat16))
-        w = weight.to(torch.bfloat16).contiguous()
         b = None if bias is None else bias.to(torch.bfloat16).contiguous()
         M, K = x.shape
-        N = w.shape[0]
+        N = weight.shape[0]
         dev = x.device
         u8 = dict(dtype=torch.uint8, device=dev)
         x8 = torch.empty((M, K), **u8)
         x8t = torch.empty((K, M), **u8)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        mode_x = layer._mode("x")
-        mode_w = layer._mode("w")
-        key = (weight.data_ptr(), weight._version, weight.dtype, str(dev), mode_w)
+        key = (weight.data_ptr(), weight._version, weight.dtype, str(dev), layer._mode("w"))
         cached = layer._w_cache if (layer.config.reuse_weight_cast and layer._w_cache is not None
                                     and layer._w_cache[0] == key) else None
+        mode_x, sx = layer._prepare("x", x)
         if cached is not None:
-            # unchanged weight: its fp8 copies and scale (in layer.sw) are still valid
-            w8, w8t = cached[1], cached[2]
+            # unchanged weight: its fp8 copies and scale (in the w state) are still valid
+            w, w8, w8t = None, cached[1], cached[2]
+            mode_w, sw = "dynamic", layer.state("w")
             layer.weight_cast_reuses += 1
         else:
             # fresh copies: an earlier forward's backward may still read the old ones
+            w = weight.to(torch.bfloat16).contiguous()
             w8 = torch.empty((N, K), **u8)
             w8t = torch.empty((K, N), **u8)
-        f8lin.forward(x, None if cached is not None else w, y, x8, x8t, w8, w8t, layer.sx, layer.sw, layer.ws,
-                      mode_x, mode_w, layer.config.amax_algo, bias=b, w_cast_valid=cached is not None)
+            mode_w, sw = layer._prepare("w", w)
+        f8lin.forward(x, w, y, x8, x8t, w8, w8t, sx, sw, layer.fp8_workspace, mode_x, mode_w,
+                      layer.config.amax_algo, bias=b, w_cast_valid=cached is not None)
         if cached is None and layer.config.reuse_weight_cast:
             layer._w_cache = (key, w8, w8t)
         # backward must use the scales these fp8 copies were made with, even if
         # the layer runs forward again before it (micro-batches, recomputation)
-        ctx.save_for_backward(x8t, w8t, layer.sx.scale.clone(), layer.sw.scale.clone())
+        ctx.save_for_backward(x8t, w8t, sx.scale.clone(), sw.scale.clone())
         ctx.layer = layer
         ctx.M0 = M0
         ctx.w_dtype = weight.dtype
@@ -111,16 +140,17 @@ class _Float8LinearFn(torch.autograd.Function):
             db_ws = f8lin.new_dbias_workspace(M, N, dev)
         # scratch for GEMMs split along their contraction (None when none splits at this shape)
         gemm_ws = f8lin.new_backward_gemm_workspace(M, N, K, dev)
+        mode_dy, sdy = layer._prepare("dy", dy)
         f8lin.backward(dy, x8t, w8t, dx, dw, dy8, dy8t, f8lin.ScaleView(sx_scale), f8lin.ScaleView(sw_scale),
-                       layer.sdy, layer.ws, layer._mode("dy"), layer.config.amax_algo, dbias=db, dbias_ws=db_ws,
+                       sdy, layer.fp8_workspace, mode_dy, layer.config.amax_algo, dbias=db, dbias_ws=db_ws,
                        gemm_ws=gemm_ws)
         return dx[:ctx.M0], dw.to(ctx.w_dtype), (None if db is None else db.to(ctx.b_dtype)), None
 
 
 class Float8Linear(nn.Module):
-    """nn.Linear (no bias) whose forward and backward GEMMs run in fp8 with
-    tensorwise scaling: X and W cast to e4m3, dY to e5m2, per-tensor scales
-    from the current amax (dynamic) or a 16-step amax history (delayed)."""
+    """nn.Linear whose forward and backward GEMMs run in fp8 with tensorwise
+    scaling: X and W cast to e4m3, dY to e5m2, per-tensor scales from the
+    current amax (dynamic) or a 16-step amax history (delayed)."""
 
     def __init__(self, in_features: int, out_features: int, config: Optional[Float8LinearConfig] = None,
                  weight: Optional[torch.Tensor] = None, device=None, dtype=torch.bfloat16, bias=False):
@@ -143,50 +173,91 @@ class Float8Linear(nn.Module):
             self.bias = nn.Parameter(torch.zeros(out_features, device=self.weight.device, dtype=self.weight.dtype))
         else:
             self.register_parameter("bias", None)
-        self._states_device = None
-        self._initialized: Dict[str, bool] = {"x": False, "w": False, "dy": False}
+        dev = self.weight.device
+        for role in _ROLES:
+            for name, shape, dt in _STATE_FIELDS:
+                self.register_buffer(f"fp8_{role}_{name}", torch.zeros(shape, dtype=dt, device=dev))
+        # the library's workspace, and one history per role whose slot 0 holds
+        # the current amax during a delayed role's first step (slots 1-15 stay 0)
+        self.register_buffer("fp8_workspace", torch.zeros(f8lin.workspace_bytes(), dtype=torch.uint8, device=dev),
+                             persistent=False)
+        self.register_buffer("fp8_seed_history", torch.zeros((len(_ROLES), f8lin.HISTORY_LEN), dtype=torch.float32,
+                                                             device=dev), persistent=False)
+        self._initialized: Dict[str, bool] = {r: False for r in _ROLES}
+        self._produced: Dict[str, bool] = {r: False for r in _ROLES}
         self._w_cache = None  # (key, w8, w8t) of the weight's last cast
         self.weight_cast_reuses = 0
 
-    # ---- scaling state (device-resident, created on first use on the weight's device)
-    def _ensure_states(self, device):
-        if self._states_device != device:
-            self.sx = f8lin.ScalingState(device)
-            self.sw = f8lin.ScalingState(device)
-            self.sdy = f8lin.ScalingState(device)
-            self.ws = f8lin.new_workspace(device)
-            self._states_device = device
-            self._initialized = {"x": False, "w": False, "dy": False}
-            self._w_cache = None
+    # ---- scaling state
+    def state(self, role: str) -> f8lin.ScalingState:
+        """The role's device state (views of this module's buffers)."""
+        return f8lin.ScalingState(tensors=tuple(getattr(self, f"fp8_{role}_{n}") for n, _, _ in _STATE_FIELDS))
+
+    sx = property(lambda self: self.state("x"))
+    sw = property(lambda self: self.state("w"))
+    sdy = property(lambda self: self.state("dy"))
 
     def _cfg(self, role):
         return {"x": self.config.cast_config_input, "w": self.config.cast_config_weight,
                 "dy": self.config.cast_config_grad_output}[role]
 
     def _mode(self, role):
-        # delayed scaling takes its first step's scale from the current amax
+        """How the role's scale is taken this step: "delayed" (from the
+        history) once the role has been synced, else "dynamic" (the current
+        tensor's amax; for a delayed role this is its first step)."""
         if self._cfg(role).scaling_type == "delayed" and self._initialized[role]:
             return "delayed"
         return "dynamic"
 
-    def delayed_states(self):
-        return [st for role, st in (("x", getattr(self, "sx", None)), ("w", getattr(self, "sw", None)),
-                                    ("dy", getattr(self, "sdy", None)))
-                if st is not None and self._cfg(role).scaling_type == "delayed"]
+    def _prepare(self, role, t: torch.Tensor):
+        """(mode, state) for casting tensor t of `role`, and marks the role as
+        having produced an amax since the last sync."""
+        self._produced[role] = True
+        st = self.state(role)
+        if self._cfg(role).scaling_type == "dynamic" or self._initialized[role]:
+            return self._mode(role), st
+        # a delayed role's first step: the delayed cast with a history seeded
+        # with this tensor's amax (the dynamic scale; the cast folds the amax
+        # into the state, max over micro-batches)
+        seed = self.fp8_seed_history[_ROLES.index(role)]
+        f8lin.amax(t, seed[0:1], self.fp8_workspace, self.config.amax_algo)
+        return "delayed", f8lin.ScalingState(tensors=(st.amax, st.scale, seed, st.hist_meta))
 
-    def _mark_synced(self):
-        for role in ("x", "w", "dy"):
-            if self._cfg(role).scaling_type == "delayed":
-                self._initialized[role] = True
-        if self._cfg("w").scaling_type == "delayed":
-            self._w_cache = None  # the history moved: the weight's scale changes
+    def delayed_states(self):
+        """States of the delayed roles that produced an amax since the last sync."""
+        return [self.state(r) for r in self._sync_roles()]
+
+    def _sync_roles(self):
+        return [r for r in _ROLES if self._cfg(r).scaling_type == "delayed" and self._produced[r]]
+
+    def _mark_synced(self, roles=None):
+        for r in (self._sync_roles() if roles is None else roles):
+            self._initialized[r] = True
+            self._produced[r] = False
+        self._w_cache = None  # the weight's scale may move with its history; the step is over
+
+    def invalidate_weight_cast(self):
+        """Drop the cached weight cast (after changing the weight through .data)."""
+        self._w_cache = None
+
+    # ---- checkpointing: the buffers are saved by nn.Module; the flags here
+    def get_extra_state(self):
+        return {"initialized": [bool(self._initialized[r]) for r in _ROLES]}
+
+    def set_extra_state(self, state):
+        flags = state["initialized"]
+        self._initialized = {r: bool(f) for r, f in zip(_ROLES, flags)}
+        self._produced = {r: False for r in _ROLES}
+        self._w_cache = None
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if not x.is_cuda:
             raise RuntimeError("Float8Linear runs on the GPU only (libf8lin has no CPU path)")
         if x.shape[-1] != self.in_features:
             raise ValueError(f"expected last dimension {self.in_features}, got {x.shape[-1]}")
-        self._ensure_states(x.device)
+        if self.fp8_x_amax.device != x.device:
+            raise RuntimeError(f"Float8Linear's scaling state is on {self.fp8_x_amax.device}, the input on "
+                               f"{x.device}: move the module with .to()")
         lead = x.shape[:-1]
         y = _Float8LinearFn.apply(x.reshape(-1, self.in_features), self.weight, self.bias, self)
         return y.reshape(*lead, self.out_features)
@@ -222,16 +293,35 @@ def convert_to_float8_training(module: nn.Module, config: Optional[Float8LinearC
     return module
 
 
-def sync_float8_amax_and_scale_history(module: nn.Module) -> None:
-    """After backward: pushes every delayed-scaling tensor's amax of this
-    step into its 16-entry history (one launch for all layers' states)."""
-    states = []
-    layers = []
+def invalidate_weight_cast(module: nn.Module) -> None:
+    """Drops every Float8Linear's cached weight cast (call it after changing
+    weights through .data when reuse_weight_cast is on)."""
     for m in module.modules():
-        if isinstance(m, Float8Linear) and m._states_device is not None:
-            states.extend(m.delayed_states())
-            layers.append(m)
+        if isinstance(m, Float8Linear):
+            m.invalidate_weight_cast()
+
+
+def sync_float8_amax_and_scale_history(module: nn.Module, check: bool = False) -> None:
+    """After backward: pushes the amax of this step of every delayed-scaling
+    role that produced one into its 16-entry history (one launch for all
+    layers' states).  check=True also reads back the library's per-state
+    status (a host synchronisation) and raises if a state's {count, pos}
+    was corrupt (such a state is left untouched)."""
+    states, layers = [], []
+    for m in module.modules():
+        if isinstance(m, Float8Linear):
+            roles = m._sync_roles()
+            states.extend(m.state(r) for r in roles)
+            layers.append((m, roles))
+    status = None
     if states:
-        f8lin.delayed_update(states)
-    for m in layers:
-        m._mark_synced()
+        if check:
+            status = torch.empty(len(states), dtype=torch.int32, device=states[0].amax.device)
+        f8lin.delayed_update(states, status=status)
+    for m, roles in layers:
+        m._mark_synced(roles)
+    if status is not None:
+        bad = torch.nonzero(status).flatten().tolist()
+        if bad:
+            raise RuntimeError(f"sync_float8_amax_and_scale_history: {len(bad)} corrupt delayed-scaling "
+                               f"state(s) (invalid count/pos), left unchanged: state indices {bad}")
