@@ -7,15 +7,22 @@ workload, through the C ABI (f8lin_forward / f8lin_backward; plus
 f8lin_delayed_update for delayed scaling), on seeded synthetic bf16 inputs
 already resident in HBM.  Prints ONE JSON line.
 
-Timed region: W untimed warm-up steps, synchronize, K timed steps bracketed
-by HIP events on the launch stream, synchronize.  Input sets rotate between
+Default workload: the pages' largest single-linear shape, 65536 x 4096 ->
+4096 with 0.1% outliers in X (pytorch/torchtitan PR #778, single-linear-layer
+table, input (65536, 4096)).
+
+Timed region: steps for --settle-ms of wall clock (the shader clock settles
+under load), W untimed warm-up steps, synchronize, K timed steps bracketed by
+HIP events on the launch stream, synchronize.  Input sets rotate between
 steps (enough copies that a step's inputs are not left in the 256 MB
 last-level cache by the previous step).
 
-A second, instrumented pass runs the same K steps through the individual
-entry points (amax / cast_transpose / gemm -- the exact launch sequence
-f8lin_forward/backward perform) with HIP events between the calls on the same
-stream, giving each kernel's average duration for the roofline figures.
+Then: the two amax algorithms in alternating timed blocks; an instrumented
+pass of the same steps with HIP events around every forward / backward call
+and the events each call records around its own GEMM launch (the roofline
+figure is the backward's dgrad + wgrad launch as f8lin_backward issues it);
+both amax algorithms alone; the epilogue amax against the amax pass it
+spares; a plain device copy for reference.
 
 The oracle (CPU, test infrastructure) is timed on the host cores on a bounded
 sample of the same workload for the cpu_baseline field.
@@ -34,27 +41,29 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20
-# P3 (pytorch/torchtitan PR #778) single-linear table, (4096, 4096) input,
-# float8nocompile ATOMIC_MAX on H100: 977.858 (read as microseconds) for
-# forward + backward of a 4096->4096 linear -> 6*4096^3 / 977.858 us.
-H100_BASELINE_TFLOPS = {"linear4096_m4096": 6 * 4096 ** 3 / 977.858e-6 / 1e12,
-                        "linear4096_m16": 6 * 16 * 4096 ** 2 / 386.469e-6 / 1e12,
-                        "linear4096_m256": 6 * 256 * 4096 ** 2 / 408.137e-6 / 1e12,
-                        "linear4096_m65536_outliers": 6 * 65536 * 4096 ** 2 / 10813.3e-6 / 1e12}
+# The pages' H100 float8nocompile ATOMIC_MAX forward + backward times for a
+# 4096 -> 4096 linear (pytorch/torchtitan PR #778, single-linear-layer table,
+# read as microseconds), by input rows: another machine's numbers, context only.
+H100_US = {"linear4096_m16": 386.469, "linear4096_m256": 408.137, "linear4096_m4096": 977.858,
+           "linear4096_m65536_outliers": 10813.3}
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="linear4096_m4096")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="linear4096_m65536_outliers")
     p.add_argument("--algo", default="twopass", choices=["atomic", "twopass"],
-                   help="amax algorithm of the timed loop; the other one is timed right after")
+                   help="amax algorithm of the headline loop")
+    p.add_argument("--settle-ms", type=float, default=1000.0,
+                   help="run steps for this long (wall clock) before the warm-up, so the clocks settle")
+    p.add_argument("--algo-rounds", type=int, default=3,
+                   help="rounds of alternating timed blocks (one per amax algorithm) for the comparison")
     p.add_argument("--rotate", type=int, default=0, help="input sets to rotate (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4096, help="rows of X/dY in the oracle's timed sample")
-    p.add_argument("--only-timed", action="store_true", help="skip the instrumented pass (for profiling)")
+    p.add_argument("--only-timed", action="store_true", help="skip everything after the headline (for profiling)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes three times (counter calibration)")
     return p.parse_args()
@@ -66,17 +75,17 @@ def sha256_of(path):
 
 
 def load_traffic(gemm_src, workload):
-    """HBM traffic of the GEMM from rocprofv3 counter runs, if the committed
-    record was taken on the current kernel source and on this workload (else
-    None)."""
+    """HBM traffic of the backward GEMM launch from rocprofv3 counter runs, if
+    the committed record for this workload was read on the current kernel
+    source (else None)."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path))
-    except (OSError, ValueError):
+        rec = json.load(open(path)).get("records", {}).get(workload)
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("source_sha256") != sha256_of(gemm_src) or rec.get("workload_name") != workload:
+    if not rec or rec.get("source_sha256") != sha256_of(gemm_src):
         return None
     return rec
 
@@ -128,60 +137,91 @@ def main():
     groups = inputs.groups_of(wl)
     assert not (delayed and any(len(g) > 1 for g in groups)), "shared inputs are measured with dynamic scaling"
 
-    def step(t, algo):
+    def step(t, algo, ev=None):
+        """One step; with ev (a list), HIP events around each forward / backward
+        call and, from inside the call, around its GEMM launch are appended as
+        (kind, begin, end, group) for the instrumented pass."""
         mode = "delayed" if (delayed and t > 0) else "dynamic"
         data = sets[t % R]
+
+        def events(kind, g):
+            if ev is None:
+                return None, None
+            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            gemm = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev.append((kind, pair, gemm, g))
+            return pair, gemm
+
         for g in groups:
+            call, gemm = events("fwd", g)
+            if call:
+                call[0].record(stream)
             if len(g) == 1:
                 buf, (l, x, w, dy) = bufs[g[0]], data[g[0]]
-                buf.forward(x, w, mode, algo)
-                buf.backward(dy, mode, algo)
-                continue
-            # linears reading one X: X cast once, their forward GEMMs in one launch
+                buf.forward(x, w, mode, algo, gemm_events=gemm)
+            else:
+                # linears reading one X: X cast once, their forward GEMMs in one launch
+                lead = bufs[g[0]]
+                f8lin.forward_shared_x(data[g[0]][1], lead.x8, lead.x8t, lead.sx, lead.ws,
+                                       [{"w": data[i][2], "y": bufs[i].y, "w8": bufs[i].w8, "w8t": bufs[i].w8t,
+                                         "sw": bufs[i].sw} for i in g], mode, algo, gemm_events=gemm)
+            if call:
+                call[1].record(stream)
             lead = bufs[g[0]]
-            x = data[g[0]][1]
-            f8lin.forward_shared_x(x, lead.x8, lead.x8t, lead.sx, lead.ws,
-                                   [{"w": data[i][2], "y": bufs[i].y, "w8": bufs[i].w8, "w8t": bufs[i].w8t,
-                                     "sw": bufs[i].sw} for i in g], mode, algo)
             for i in g:
                 b = bufs[i]
+                call, gemm = events("bwd", [i])
+                if call:
+                    call[0].record(stream)
                 f8lin.backward(data[i][3], lead.x8t, b.w8t, b.dx, b.dw, b.dy8, b.dy8t, lead.sx, b.sw, b.sdy, b.ws,
-                               mode, algo)
+                               mode, algo, gemm_ws=b.gemm_ws, gemm_events=gemm)
+                if call:
+                    call[1].record(stream)
         if delayed:
             # the history sync after backward: one call for every linear's states
             f8lin.delayed_update([st for b in bufs for st in b.states()])
 
-    def timed_steps(algo):
-        for t in range(args.warmup):
-            step(t, algo)
+    t_next = [0]  # step counter across phases (delayed workloads use it for the mode)
+
+    def run(n, algo):
+        for _ in range(n):
+            step(t_next[0], algo)
+            t_next[0] += 1
+
+    def timed(n, algo):
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        t_host0 = time.perf_counter()
         e0.record(stream)
-        for t in range(args.steps):
-            step(args.warmup + t, algo)
+        run(n, algo)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t_host0
+        return e0.elapsed_time(e1) / n
 
-    def step_spread(algo, n=100):
-        """Per-step HIP events around n further steps: median and min (the
-        events themselves add a little time per step)."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for t, (a, b) in enumerate(evs):
-            a.record(stream)
-            step(args.warmup + args.steps + t, algo)
-            b.record(stream)
+    # ---- settle: the shader clock takes ~0.1 s of load to reach its sustained
+    # level; run steps for settle_ms of wall clock first
+    t0 = time.perf_counter()
+    settle_steps = 0
+    while True:
+        run(5, args.algo)
+        settle_steps += 5
         torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) for a, b in evs)
-        return ts[len(ts) // 2], ts[0]
+        if (time.perf_counter() - t0) * 1e3 >= args.settle_ms:
+            break
+    settle_ms = (time.perf_counter() - t0) * 1e3
 
-    # ---- timed region (the headline), then the same with the other amax algorithm
-    ms_per_step, t_host = timed_steps(args.algo)
-    ms_median, ms_min = step_spread(args.algo)
-    other = "twopass" if args.algo == "atomic" else "atomic"
-    ms_other = None if (delayed or args.only_timed) else timed_steps(other)[0]
+    # ---- timed region (the headline): W warm-up steps, then exactly K steps
+    run(args.warmup, args.algo)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_host0 = time.perf_counter()
+    e0.record(stream)
+    run(args.steps, args.algo)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
     flops = wl.flops
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
@@ -195,43 +235,64 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": (round(tflops / H100_BASELINE_TFLOPS[args.workload], 3)
-                        if args.workload in H100_BASELINE_TFLOPS else None),
+        "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
                    "shared_input_groups": [list(g) for g in wl.shared_x],
                    "linears": [{"name": l.name, "M": l.M, "K": l.K, "N": l.N} for l in wl.linears],
                    "scaling": wl.scaling, "amax_algo": args.algo, "rotating_input_sets": R,
-                   "inputs": "X~N(0,1), W~N(0,1/K), dY~N(0,1e-3) bf16, seeded"},
+                   "inputs": "X~N(0,1), W~N(0,1/K), dY~N(0,1e-3) bf16, seeded"
+                             + (f"; {wl.outlier_fraction:.1%} of X x{wl.outlier_multiplier:g}"
+                                if wl.outlier_fraction else "")},
         "fwd_bwd_us": round(ms_per_step * 1e3, 2),
-        "fwd_bwd_us_per_step_events": {"median": round(ms_median * 1e3, 2), "min": round(ms_min * 1e3, 2),
-                                       "steps": 100},
         "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps,
+                   "what": "untimed steps run for this wall-clock time before the warm-up (clock settling)"},
         "host_wall_s_timed": round(t_host, 4),
     }
-    if ms_other is not None:
-        out["fwd_bwd_us_by_amax_algo"] = {args.algo: round(ms_per_step * 1e3, 2), other: round(ms_other * 1e3, 2)}
-    if out["vs_baseline"] is not None:
-        out["baseline_note"] = ("pages' H100 float8nocompile ATOMIC_MAX fwd+bwd time for this shape "
-                                "(read as microseconds), converted to TFLOP/s; another machine's number")
+    if args.workload in H100_US:
+        h100_us = H100_US[args.workload]
+        out["h100_context"] = {"fwd_bwd_us": h100_us, "tflops": round(flops / (h100_us * 1e-6) / 1e12, 1),
+                               "what": "the pages' H100 float8nocompile ATOMIC_MAX figure for this shape (single-"
+                                       "linear table, read as microseconds): another machine, context only"}
 
-    if not args.only_timed:
-        out.update(instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed))
-        # the step's dominant kernel: the backward's dgrad + wgrad launch
-        rl = out["kernels"]["gemm_bwd_pair"]
-        traffic = load_traffic(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "csrc", "gemm.hip"),
-                               args.workload)
-        out["roofline"] = {"kernel": "gemm_fp8_tn_kernel<e5m2,e4m3> (dgrad + wgrad, one launch)",
-                           "bound": "mfma", "achieved": rl["tflops"],
-                           "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(rl["tflops"] / PEAK_FP8_TFLOPS, 4),
-                           "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None),
-                           "algorithmic_bytes_per_launch": rl["algorithmic_bytes_per_launch"]}
-        if traffic:
-            out["roofline"]["traffic_note"] = traffic.get("note", "")
-        out["hbm_copy_reference"] = copy_reference(torch, stream)
+    if args.only_timed:
+        print(json.dumps(out), flush=True)
+        return
 
+    # ---- the two amax algorithms, in alternating timed blocks after the same settle
+    if not delayed:
+        blocks = {"atomic": [], "twopass": []}
+        nb = max(args.steps, 10)
+        for r in range(args.algo_rounds):
+            order = ("twopass", "atomic") if r % 2 == 0 else ("atomic", "twopass")
+            for algo in order:
+                run(2, algo)  # the first steps after a switch are not timed
+                blocks[algo].append(timed(nb, algo) * 1e3)
+        out["fwd_bwd_us_by_amax_algo"] = {
+            a: {"median_us": round(float(np.median(v)), 2), "blocks_us": [round(x, 2) for x in v]}
+            for a, v in blocks.items()}
+        out["fwd_bwd_us_by_amax_algo"]["what"] = (f"{args.algo_rounds} rounds of one {nb}-step block per algorithm, "
+                                                  "alternating which goes first")
+
+    out.update(instrumented(args, wl, bufs, sets, step, t_next, f8lin, torch, stream, delayed))
+    rl = out["kernels"]["gemm_bwd"]
+    traffic = load_traffic(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "csrc", "gemm.hip"),
+                           args.workload)
+    out["roofline"] = {"kernel": rl["kernel"], "bound": "mfma", "achieved": rl["tflops"],
+                       "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(rl["tflops"] / PEAK_FP8_TFLOPS, 4),
+                       "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None),
+                       "algorithmic_bytes_per_launch": rl["algorithmic_bytes_per_launch"],
+                       "flops_per_launch": rl["flops_per_launch"],
+                       "timing": "HIP events that f8lin_backward records on its stream around the GEMM launch it "
+                                 "issues (ev_gemm_begin / ev_gemm_end), averaged over the instrumented steps"}
+    if traffic:
+        out["roofline"]["traffic_note"] = traffic.get("note", "")
+    if not delayed:
+        out["epilogue_amax"] = epilogue_amax(wl, bufs, sets, f8lin, torch, stream)
+    out["hbm_copy_reference"] = copy_reference(torch, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, wl, sets, np, torch)
     print(json.dumps(out), flush=True)
@@ -261,73 +322,66 @@ def copy_reference(torch, stream, nbytes=1 << 30, reps=20):
             "us_per_copy": round(us, 2), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
-    """Per-call and per-kernel durations with HIP events on the launch stream:
-    each f8lin_forward / f8lin_backward call as the step issues it, and its
-    GEMM launch again on its own (f8lin_gemm; f8lin_gemm_batch for the
-    backward's dgrad + wgrad pair).  A call's time minus its GEMM's is its
-    amax + cast phase, whose algorithmic bytes are 2 B/element for each
-    dynamic-mode amax pass and 4 B/element for each cast.  f8lin_gemm_batch
-    is the plain shared launch: where f8lin_backward splits a GEMM along K or
-    hands out the pair's tiles through its work queue (problems of different
-    contraction length), the pair inside the call runs faster than this
-    figure and the amax + cast share absorbs the difference; the step time
-    above is the real path either way.  At M = N = K the two launches are the
-    same."""
-    acc = {k: [0.0, 0, 0.0] for k in ("fwd_call", "bwd_call", "gemm_fwd", "gemm_bwd_pair")}  # ms, calls, units
-    ew_bytes = {"fwd": 0, "bwd": 0}
-    gemm_bytes = {"gemm_fwd": [], "gemm_bwd_pair": []}
-
-    def timed(kind, fn, units):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        fn()
-        b.record(stream)
-        pending.append((kind, a, b, units))
-
-    # the timed loops ran just before, so the device is warm: fewer rounds
-    # suffice.  Everything is queued before one synchronisation, so the host
-    # stays ahead of the GPU and no call starts from an idle device.
-    warm, steps = min(args.warmup, 10), min(args.steps, 100)
+def instrumented(args, wl, bufs, sets, step, t_next, f8lin, torch, stream, delayed):
+    """Per-call and per-GEMM durations of the real step, with HIP events on
+    the launch stream: around each f8lin_forward / f8lin_backward call as the
+    step issues it, and the events each call records around its own GEMM
+    launch (so the GEMM figures are those of the launches the path issues:
+    the backward's work-queue or split launches included).  A call's time
+    minus its GEMM's is its amax + cast phase, whose algorithmic bytes are
+    2 B/element for each dynamic-mode amax pass and 4 B/element for each
+    cast.  Then both amax algorithms alone (f8lin_amax) on the step's
+    tensors."""
+    lin = wl.linears
+    warm, steps = 2, min(max(args.steps, 5), 20)
     recorded = []
     for t in range(warm + steps):
-        pending = []
-        mode = "delayed" if (delayed and t > 0) else "dynamic"
-        for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
-            per = 6 if mode == "dynamic" else 4  # amax pass (dynamic) + cast
-            timed("fwd_call", lambda: buf.forward(x, w, mode, args.algo), per * (l.M * l.K + l.N * l.K))
-            timed("gemm_fwd", lambda: f8lin.gemm(buf.x8, "e4m3", buf.w8, "e4m3", buf.sx.inv_scale,
-                                                 buf.sw.inv_scale, buf.y), 2 * l.M * l.N * l.K)
-            timed("bwd_call", lambda: buf.backward(dy, mode, args.algo), per * l.M * l.N)
-            # dgrad and wgrad in one launch, as f8lin_backward issues them
-            timed("gemm_bwd_pair", lambda: f8lin.gemm_batch(
-                [(buf.dy8, buf.w8t, buf.sdy.inv_scale, buf.sw.inv_scale, buf.dx),
-                 (buf.dy8t, buf.x8t, buf.sdy.inv_scale, buf.sx.inv_scale, buf.dw)], "e5m2", "e4m3"),
-                4 * l.M * l.N * l.K)
-            if delayed:
-                f8lin.delayed_update(buf.states())
-            if t == 0:
-                gemm_bytes["gemm_fwd"].append(l.M * l.K + l.N * l.K + 2 * l.M * l.N)
-                gemm_bytes["gemm_bwd_pair"].append(l.M * l.N + l.N * l.K + 2 * l.M * l.K +
-                                                   l.M * l.N + l.M * l.K + 2 * l.N * l.K)
+        ev = []
+        step(t_next[0], args.algo, ev)
+        mode = "delayed" if (delayed and t_next[0] > 0) else "dynamic"
+        t_next[0] += 1
         if t >= warm:
-            recorded.extend(pending)
+            recorded.append((ev, mode))
     torch.cuda.synchronize()
-    for kind, a, b, units in recorded:
-        acc[kind][0] += a.elapsed_time(b)
-        acc[kind][1] += 1
-        acc[kind][2] += units
+    acc = {k: [0.0, 0, 0.0, 0.0] for k in ("fwd_call", "bwd_call", "gemm_fwd", "gemm_bwd")}  # ms, n, work, bytes
+    for ev, mode in recorded:
+        per = 6 if mode == "dynamic" else 4  # amax pass (dynamic) + cast, bytes per element
+        for kind, call, gemm, g in ev:
+            t_call = call[0].elapsed_time(call[1])
+            t_gemm = gemm[0].elapsed_time(gemm[1])
+            ls = [lin[i] for i in g]
+            if kind == "fwd":
+                l0 = ls[0]
+                cast_b = per * (l0.M * l0.K + sum(l.N * l.K for l in ls))  # X once, each W
+                gflop = sum(2 * l.M * l.N * l.K for l in ls)
+                gbytes = sum(l.M * l.K + l.N * l.K + 2 * l.M * l.N for l in ls)
+                key = "fwd"
+            else:
+                l = ls[0]
+                cast_b = per * l.M * l.N
+                gflop = 4 * l.M * l.N * l.K
+                gbytes = (l.M * l.N + l.N * l.K + 2 * l.M * l.K) + (l.M * l.N + l.M * l.K + 2 * l.N * l.K)
+                key = "bwd"
+            a = acc[key + "_call"]
+            a[0] += t_call
+            a[1] += 1
+            a[2] += cast_b
+            b = acc["gemm_" + key]
+            b[0] += t_gemm
+            b[1] += 1
+            b[2] += gflop
+            b[3] += gbytes
     k = {}
-    for name in ("gemm_fwd", "gemm_bwd_pair"):
-        ms, n, el = acc[name]
-        k[name] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
-                   "tflops": round(el / (ms * 1e-3) / 1e12, 2),
-                   "algorithmic_bytes_per_launch": int(sum(gemm_bytes[name]) / len(gemm_bytes[name])),
-                   "flops_per_launch": int(el / n)}
-    for side, gemm in (("fwd", "gemm_fwd"), ("bwd", "gemm_bwd_pair")):
-        ms_call, n, by = acc[side + "_call"]
-        ms_ew = ms_call - acc[gemm][0]
+    for name, kern in (("gemm_fwd", "gemm_fp8_tn_kernel<e4m3,e4m3> (forward; one launch per call)"),
+                       ("gemm_bwd", "gemm_fp8_tn_kernel<e5m2,e4m3> (dgrad + wgrad, the launch f8lin_backward "
+                                    "issues)")):
+        ms, n, fl, by = acc[name]
+        k[name] = {"kernel": kern, "avg_us": round(ms / n * 1e3, 3), "launches": n,
+                   "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                   "algorithmic_bytes_per_launch": int(by / n), "flops_per_launch": int(fl / n)}
+    for side in ("fwd", "bwd"):
+        ms_call, n, by, _ = acc[side + "_call"]
+        ms_ew = ms_call - acc["gemm_" + side][0]
         k["amax_cast_" + side] = {"avg_us": round(ms_ew / n * 1e3, 3), "calls": n,
                                   "call_avg_us": round(ms_call / n * 1e3, 3),
                                   "gbs": round(by / (ms_ew * 1e-3) / 1e9, 1),
@@ -335,32 +389,69 @@ def instrumented(args, wl, sets, bufs, R, f8lin, torch, stream, delayed):
                                   "algorithmic_bytes_per_call": int(by / n),
                                   "what": ("amax pass(es) + cast of X and W" if side == "fwd" else
                                            "amax pass + cast of dY") + " = call time minus its GEMM launch"}
-    # amax alone, both algorithms, on the step's three tensors
-    for algo in ("atomic", "twopass"):
-        tot_ms, n, el = 0.0, 0, 0
-        kept = []
-        for t in range(warm + steps):
-            evs = []
-            for buf, (l, x, w, dy) in zip(bufs, sets[t % R]):
-                for tensor, st in ((x, buf.sx), (w, buf.sw), (dy, buf.sdy)):
+    # amax alone, both algorithms, alternating, on the step's X, W and dY (first input set)
+    per_algo = {"atomic": [0.0, 0, 0], "twopass": [0.0, 0, 0]}
+    word = torch.zeros(1, dtype=torch.float32, device=bufs[0].ws.device)
+    pend = []
+    for rep in range(12):
+        for algo in (("atomic", "twopass") if rep % 2 == 0 else ("twopass", "atomic")):
+            for b, (_, x, w, dy) in zip(bufs, sets[0]):
+                for tensor in (x, w, dy):
                     a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
+                    e = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
-                    f8lin.amax(tensor, st.amax, buf.ws, algo)
-                    b.record(stream)
-                    evs.append((a, b, tensor.numel()))
-            if t >= warm:
-                kept.extend(evs)
-        torch.cuda.synchronize()
-        for a, b, units in kept:
-            tot_ms += a.elapsed_time(b)
-            n += 1
-            el += units
-        k["amax_" + algo] = {"avg_us": round(tot_ms / n * 1e3, 3), "launches": n,
-                             "gbs": round(2 * el / (tot_ms * 1e-3) / 1e9, 1),
-                             "frac_hbm_peak": round(2 * el / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "bytes_per_elem": 2}
+                    f8lin.amax(tensor, word, b.ws, algo)
+                    e.record(stream)
+                    if rep >= 2:
+                        pend.append((algo, a, e, tensor.numel()))
+    torch.cuda.synchronize()
+    for algo, a, e, n in pend:
+        v = per_algo[algo]
+        v[0] += a.elapsed_time(e)
+        v[1] += 1
+        v[2] += n
+    for algo, (ms, n, el) in per_algo.items():
+        k["amax_" + algo] = {"avg_us": round(ms / n * 1e3, 3), "launches": n,
+                             "gbs": round(2 * el / (ms * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(2 * el / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "bytes_per_elem": 2,
+                             "what": "f8lin_amax alone on the step's X, W and dY, the algorithms alternating"}
     return {"kernels": k}
+
+
+def epilogue_amax(wl, bufs, sets, f8lin, torch, stream, reps=12):
+    """The amax taken in the GEMM epilogue (y_amax) against the amax pass it
+    spares the next layer, on the workload's first linear: the forward call
+    with and without x_amax_given (its X amax already in the state), and the
+    forward GEMM launch with and without y_amax.  Alternating, events on the
+    launch stream."""
+    l, x, w, _ = sets[0][0]
+    b = bufs[0]
+    word = torch.zeros(1, dtype=torch.float32, device=x.device)
+    f8lin.forward(x, w, b.y, b.x8, b.x8t, b.w8, b.w8t, b.sx, b.sw, b.ws, algo="twopass")  # sx.amax = amax(X)
+    res = {"call": [], "call_given": [], "gemm": [], "gemm_y_amax": []}
+    pend = []
+    for r in range(reps):
+        for given in ((False, True) if r % 2 == 0 else (True, False)):
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            c0.record(stream)
+            f8lin.forward(x, w, b.y, b.x8, b.x8t, b.w8, b.w8t, b.sx, b.sw, b.ws, algo="twopass",
+                          x_amax_given=given, gemm_events=g, y_amax=word if given else None)
+            c1.record(stream)
+            if r >= 2:
+                pend.append((given, c0, c1, g))
+    torch.cuda.synchronize()
+    for given, c0, c1, g in pend:
+        res["call_given" if given else "call"].append(c0.elapsed_time(c1) * 1e3)
+        res["gemm_y_amax" if given else "gemm"].append(g[0].elapsed_time(g[1]) * 1e3)
+    avg = {k: round(sum(v) / len(v), 3) for k, v in res.items()}
+    return {"linear": {"name": l.name, "M": l.M, "K": l.K, "N": l.N},
+            "fwd_call_us": avg["call"], "fwd_call_us_x_amax_given": avg["call_given"],
+            "x_amax_pass_saved_us": round(avg["call"] - avg["call_given"], 3),
+            "gemm_fwd_us": avg["gemm"], "gemm_fwd_us_with_y_amax": avg["gemm_y_amax"],
+            "what": "forward call with X's amax pass vs with amax(X) handed in (x_amax_given), and its GEMM launch "
+                    "without vs with the epilogue amax of Y (y_amax); alternating calls, HIP events"}
 
 
 def cpu_baseline(args, wl, sets, np, torch):
