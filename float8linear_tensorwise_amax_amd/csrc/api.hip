@@ -16,9 +16,16 @@
 #include <string.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "device_common.h"
 #include "internal.h"
+
+// Scratch of f8lin_backward_noalloc (see static_scratch below): the
+// workspace words, then one 16 MiB region.
+constexpr size_t kStaticRegionBytes = (size_t)16 << 20;
+constexpr size_t kStaticScratchBytes = f8lin::kWorkspaceBytes + kStaticRegionBytes;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace f8lin {
 namespace {
@@ -282,9 +289,59 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
 // gradient reduces (one when dY has no rows: that tile's sums are zeros).
 int64_t dbias_tiles(int64_t M) { return M > 0 ? (M + kCastTile - 1) / kCastTile : 1; }
 
-// The backward: validation of every argument, then the launches.
-int backward_impl(const f8lin_bwd_args &in, void *stream) {
-  const f8lin_bwd_args a = in;
+// ---- Scratch of f8lin_backward_noalloc, for callers that cannot allocate
+// (code under HIP graph capture, serving loops, harnesses that forbid
+// hipMalloc).  A file-scope device array: every GPU the library runs on holds
+// its own copy, at its own address, until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and is kept per device.
+//   [0, kWorkspaceBytes)       the workspace words (atomic-amax slots and
+//                              tickets, two-pass partials, work-queue counters)
+//   [kWorkspaceBytes, +16 MiB) the bias gradient's column sums, then the
+//                              split GEMMs' fp32 partials (one after the other
+//                              in stream order)
+constexpr int kMaxDevices = 64;
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+  for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += (int)(gridDim.x * blockDim.x)) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's device address on the current device.  The first call on a
+// device looks it up and clears the workspace words on `s` with a kernel
+// (the array starts zeroed when the code object loads; every call leaves
+// those words at zero again).
+int static_scratch(uint8_t **out, hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return F8LIN_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(::scratch)) != hipSuccess || p == nullptr) return F8LIN_EHIP;
+    zero_words_kernel<<<4, 256, 0, s>>>(reinterpret_cast<uint32_t *>(p), (int)(kWorkspaceBytes / 4));
+    if (hipGetLastError() != hipSuccess) return F8LIN_EHIP;
+    g_scratch_ptr[dev] = reinterpret_cast<uint8_t *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return F8LIN_OK;
+}
+
+// The backward.  lib_scratch: the caller passes no workspace, no bias-
+// gradient scratch and no split scratch (all three must be NULL); the
+// library's static scratch on the current device takes their place (the
+// workspace words, and one region that the bias gradient's column sums and
+// the split GEMMs' partials share: the sums are consumed by the dbias kernel
+// before the GEMM launch writes any partial).
+int backward_impl(const f8lin_bwd_args &in, void *stream, bool lib_scratch) {
+  f8lin_bwd_args a = in;
+  if (lib_scratch) {
+    if (a.ws || a.dbias_ws || a.gemm_ws) return F8LIN_EINVAL;
+    if (bad_dim(a.M) || bad_dim(a.N) || bad_dim(a.K)) return F8LIN_ESHAPE;
+    if (a.dbias && f8lin_dbias_workspace_bytes(a.M, a.N) > kStaticRegionBytes) return F8LIN_EWORKSPACE;
+  }
   if (!a.sx.scale || !a.sw.scale) return F8LIN_EINVAL;
   F8_TRY(check_mode(a.mode_dy));
   F8_TRY(check_algo(a.algo));
@@ -310,10 +367,10 @@ int backward_impl(const f8lin_bwd_args &in, void *stream) {
   if (dy_given && a.mode_dy != F8LIN_DYNAMIC) return F8LIN_EINVAL;
   if (!aligned4(a.dx_amax)) return F8LIN_EALIGN;
   const bool need_ws = a.mode_dy == F8LIN_DYNAMIC && !dy_given;
-  if (need_ws) F8_TRY(check_ws(a.ws, a.ws_bytes));
-  const bool use_ws = need_ws || check_ws(a.ws, a.ws_bytes) == F8LIN_OK;
+  if (need_ws && !lib_scratch) F8_TRY(check_ws(a.ws, a.ws_bytes));
+  const bool use_ws = lib_scratch || need_ws || check_ws(a.ws, a.ws_bytes) == F8LIN_OK;
   const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
-  if (db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
+  if (!lib_scratch && db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
   const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
   const Range outs[11] = {{a.dx, 2 * mk},
                           {a.dw, 2 * nk},
@@ -321,9 +378,9 @@ int backward_impl(const f8lin_bwd_args &in, void *stream) {
                           {a.dy8t, mn},
                           {a.sdy.scale, 8},
                           {a.sdy.amax, dy_given ? 0 : 4},
-                          {a.ws, use_ws ? (int64_t)kWorkspaceBytes : 0},
+                          {a.ws, use_ws && !lib_scratch ? (int64_t)kWorkspaceBytes : 0},
                           {a.dbias, a.dbias ? 2 * a.N : 0},
-                          {a.dbias_ws, db_ws},
+                          {a.dbias_ws, lib_scratch ? 0 : db_ws},
                           {a.gemm_ws, gemm_ws},
                           {a.dx_amax, a.dx_amax ? 4 : 0}};
   const Range ins[7] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
@@ -332,6 +389,19 @@ int backward_impl(const f8lin_bwd_args &in, void *stream) {
   if (any_overlap(outs, 11, ins, 7)) return F8LIN_EINVAL;
 
   hipStream_t s = (hipStream_t)stream;
+  int64_t gemm_ws_use = gemm_ws;
+  if (lib_scratch) {  // every argument is valid: set up (first call on this device) and use the scratch
+    uint8_t *sp = nullptr;
+    F8_TRY(static_scratch(&sp, s));
+    a.ws = sp;
+    a.ws_bytes = kWorkspaceBytes;
+    uint8_t *region = sp + kWorkspaceBytes;
+    a.dbias_ws = a.dbias ? reinterpret_cast<float *>(region) : nullptr;
+    a.dbias_ws_bytes = a.dbias ? kStaticRegionBytes : 0;
+    a.gemm_ws = region;
+    a.gemm_ws_bytes = kStaticRegionBytes;
+    gemm_ws_use = (int64_t)std::min<size_t>(kStaticRegionBytes, f8lin_backward_gemm_workspace_bytes(a.M, a.N, a.K));
+  }
   uint32_t *ws = (uint32_t *)a.ws;
   CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
   if (a.dbias) cdy.colsum = a.dbias_ws;  // the cast also sums dY's columns per 128-row tile
@@ -353,7 +423,7 @@ int backward_impl(const f8lin_bwd_args &in, void *stream) {
                    {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
   g[0].amax_out = a.dx_amax;
   F8_TRY(record(a.ev_gemm_begin, s));
-  F8_TRY(status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws,
+  F8_TRY(status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws_use,
                                 use_ws ? ws + kWsQueueOffset : nullptr)));
   return record(a.ev_gemm_end, s);
 }
@@ -457,7 +527,12 @@ int f8lin_forward_shared_x(const f8lin_fwd_args *args, int count, void *stream) 
 
 int f8lin_backward(const f8lin_bwd_args *p, void *stream) {
   if (!p) return F8LIN_EINVAL;
-  return backward_impl(*p, stream);
+  return backward_impl(*p, stream, false);
+}
+
+int f8lin_backward_noalloc(const f8lin_bwd_args *p, void *stream) {
+  if (!p) return F8LIN_EINVAL;
+  return backward_impl(*p, stream, true);
 }
 
 int f8lin_delayed_update(const f8lin_state *states, int n_states, int32_t *status, void *stream) {

@@ -83,9 +83,10 @@ _lib.f8lin_gemm_batch.argtypes = [ctypes.POINTER(GemmDesc), _int, _int, _int, _v
 _lib.f8lin_forward.argtypes = [ctypes.POINTER(FwdArgs), _vp]
 _lib.f8lin_forward_shared_x.argtypes = [ctypes.POINTER(FwdArgs), _int, _vp]
 _lib.f8lin_backward.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+_lib.f8lin_backward_noalloc.argtypes = [ctypes.POINTER(BwdArgs), _vp]
 _lib.f8lin_delayed_update.argtypes = [ctypes.POINTER(State), _int, _vp, _vp]
 for _name in ("f8lin_amax", "f8lin_cast_transpose", "f8lin_cast_f32", "f8lin_gemm", "f8lin_forward",
-              "f8lin_backward", "f8lin_delayed_update"):
+              "f8lin_backward", "f8lin_backward_noalloc", "f8lin_delayed_update"):
     getattr(_lib, _name).restype = _int
 
 
@@ -329,6 +330,30 @@ def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState
                 *((None, None) if gemm_events is None else (_event(gemm_events[0]), _event(gemm_events[1]))),
                 _amax_word(dx_amax), 1 if dy_amax_given else 0)
     _check(_lib.f8lin_backward(ctypes.byref(a), _stream(stream)))
+
+
+def backward_noalloc(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState, sdy: ScalingState,
+                     mode_dy="dynamic", algo="atomic", stream=None, dbias=None, gemm_events=None, dx_amax=None,
+                     dy_amax_given=False):
+    """backward() for callers that cannot allocate: no workspace, bias-gradient
+    scratch or split scratch is passed; the library's static per-device scratch
+    (8 KB + 16 MiB) takes their place.  Calls that overlap in time on one GPU race."""
+    M, N = dy.shape
+    K = x8t.shape[0]
+    if tuple(dx.shape) != (M, K) or tuple(dw.shape) != (N, K) or tuple(w8t.shape) != (K, N):
+        raise ValueError("backward_noalloc: shape mismatch")
+    if dbias is not None and tuple(dbias.shape) != (N,):
+        raise ValueError("backward_noalloc: dbias must have shape (N,)")
+    a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr(x8t, torch.uint8), _ptr(w8t, torch.uint8),
+                _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr(dy8t, torch.uint8),
+                sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], None, 0,
+                None if dbias is None else _ptr(dbias, torch.bfloat16), None, 0, None, 0,
+                *((None, None) if gemm_events is None else (_event(gemm_events[0]), _event(gemm_events[1]))),
+                _amax_word(dx_amax), 1 if dy_amax_given else 0)
+    _check(_lib.f8lin_backward_noalloc(ctypes.byref(a), _stream(stream)))
+
+
+NOALLOC_REGION_BYTES = 16 << 20  # the static scratch's region for bias-gradient sums and split partials
 
 
 def delayed_update(states: Sequence[ScalingState], stream=None, status: Optional[torch.Tensor] = None):

@@ -314,6 +314,26 @@ int f8lin_forward_shared_x(const f8lin_fwd_args *args, int count, void *stream);
  * without enough dbias_ws); EHIP if a launch fails. */
 int f8lin_backward(const f8lin_bwd_args *args, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * backward of f8lin_backward with no workspace from the caller.  args->ws,
+ * args->dbias_ws and args->gemm_ws must be NULL; the library's own static
+ * device scratch on the current device (8 KB of workspace words plus one
+ * 16 MiB region, held by every GPU the library runs on until the process
+ * ends) takes their place: the bias gradient's column sums and the split
+ * GEMMs' partials share the region (GEMMs whose partials do not fit run
+ * unsplit, as with a gemm_ws of 16 MiB).  `stream` must belong to the
+ * current device.  Outputs equal, bit for bit, those of f8lin_backward
+ * given a zeroed workspace, a dbias_ws and a 16 MiB gemm_ws.  Every call on
+ * one GPU shares that scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race; order them.  The first call on a device
+ * looks the scratch up and clears its workspace words with a kernel on
+ * `stream`; no call allocates.
+ * Errors: as f8lin_backward; also EINVAL if ws, dbias_ws or gemm_ws is
+ * given, and EWORKSPACE if the bias gradient's column sums
+ * (f8lin_dbias_workspace_bytes(M, N)) exceed 16 MiB. */
+int f8lin_backward_noalloc(const f8lin_bwd_args *args, void *stream);
+
 /* After backward, the sync step of delayed scaling
  * (pytorch/ao issue #1297, repro script: sync_float8_amax_and_scale_history
  * after loss.backward()), for each of the n_states states:
