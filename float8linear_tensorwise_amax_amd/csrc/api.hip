@@ -130,23 +130,28 @@ int validate_cast(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mo
   if (missing(x, rows * cols) || missing(q, rows * cols)) return F8LIN_EINVAL;
   if (!aligned16(x) || !aligned16(q) || (qt && !aligned16(qt))) return F8LIN_EALIGN;
   const int64_t n = rows * cols;
-  const Range outs[3] = {{q, n}, {qt, qt ? n : 0}, {st->scale, 8}};
+  const Range outs[3] = {{q, n}, {qt, qt ? cols * transposed_ld(rows) : 0}, {st->scale, 8}};
   const Range ins[3] = {{x, 2 * n}, {st->amax, 4}, {st->history, mode == F8LIN_DELAYED ? 64 : 0}};
   if (any_overlap(outs, 3, ins, 3)) return F8LIN_EINVAL;
   return F8LIN_OK;
 }
 
 int validate_gemm(const uint8_t *a, int fa, const uint8_t *b, int fb, int64_t M, int64_t N, int64_t K,
-                  const float *ia, const float *ib, const uint16_t *c) {
+                  const float *ia, const float *ib, const uint16_t *c, int64_t lda = 0, int64_t ldb = 0) {
   if (!ia || !ib) return F8LIN_EINVAL;
   F8_TRY(check_fmt(fa));
   F8_TRY(check_fmt(fb));
   if (bad_dim(M) || bad_dim(N) || bad_dim(K) || M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems)
     return F8LIN_ESHAPE;
+  if (lda == 0) lda = K;
+  if (ldb == 0) ldb = K;
+  // a row stride: at least K, a multiple of 16, at most kMaxDim + 128 (32-bit tile offsets)
+  if (lda < K || ldb < K || lda % 16 || ldb % 16 || lda > kMaxDim + kTransposePad || ldb > kMaxDim + kTransposePad)
+    return F8LIN_ESHAPE;
   if (missing(a, M * K) || missing(b, N * K) || missing(c, M * N)) return F8LIN_EINVAL;
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return F8LIN_EALIGN;
   const Range outs[1] = {{c, 2 * M * N}};
-  const Range ins[4] = {{a, M * K}, {b, N * K}, {ia, 4}, {ib, 4}};
+  const Range ins[4] = {{a, M * lda}, {b, N * ldb}, {ia, 4}, {ib, 4}};
   if (any_overlap(outs, 1, ins, 4)) return F8LIN_EINVAL;
   return F8LIN_OK;
 }
@@ -173,7 +178,7 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
   Range outs[4 + 6 * kMaxGemms + 1], ins[2 + 6 * kMaxGemms];
   int no = 0, ni = 0;
   outs[no++] = {a0.x8, mk};
-  outs[no++] = {a0.x8t, mk};
+  outs[no++] = {a0.x8t, K * transposed_ld(M)};
   outs[no++] = {a0.sx.scale, 8};
   if (x_given)
     ins[ni++] = {a0.sx.amax, 4};
@@ -197,7 +202,7 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
       F8_TRY(check_state(a.sw, a.mode_w));
     }
     if (bad_dim(a.N) || a.N * K > kMaxElems || M * a.N > kMaxElems) return F8LIN_ESHAPE;
-    const int64_t nk = a.N * K, mn = M * a.N;
+    const int64_t nk = a.N * K, mn = M * a.N, nkt = K * transposed_ld(a.N);
     if ((!reuse && missing(a.w, nk)) || missing(a.w8, nk) || missing(a.w8t, nk) || missing(a.y, mn))
       return F8LIN_EINVAL;
     if ((!reuse && !aligned16(a.w)) || !aligned16(a.y) || !aligned16(a.w8) || !aligned16(a.w8t) ||
@@ -207,12 +212,12 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
     outs[no++] = {a.y_amax, a.y_amax ? 4 : 0};
     if (reuse) {
       ins[ni++] = {a.w8, nk};
-      ins[ni++] = {a.w8t, nk};
+      ins[ni++] = {a.w8t, nkt};
       ins[ni++] = {a.sw.scale, 8};
     } else {
       need_ws = need_ws || a.mode_w == F8LIN_DYNAMIC;
       outs[no++] = {a.w8, nk};
-      outs[no++] = {a.w8t, nk};
+      outs[no++] = {a.w8t, nkt};
       outs[no++] = {a.sw.scale, 8};
       outs[no++] = {a.sw.amax, 4};
       ins[ni++] = {a.w, 2 * nk};
@@ -241,12 +246,14 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
     if (a0.mode_x == mode) {
       given[nt] = x_given;
       ct[nt] = CastTensor{a0.x, M, K, &a0.sx, a0.x8, a0.x8t};
+      ct[nt].ldt = transposed_ld(M);
       modes[nt++] = mode;
     }
     for (int i = 0; i < count; ++i) {
       const f8lin_fwd_args &a = list[i];
       if (!a.w_cast_valid && a.mode_w == mode) {
         ct[nt] = CastTensor{a.w, a.N, K, &a.sw, a.w8, a.w8t};
+        ct[nt].ldt = transposed_ld(a.N);
         modes[nt++] = mode;
       }
     }
@@ -372,10 +379,11 @@ int backward_impl(const f8lin_bwd_args &in, void *stream, bool lib_scratch) {
   const int64_t db_ws = a.dbias ? (int64_t)f8lin_dbias_workspace_bytes(a.M, a.N) : 0;
   if (!lib_scratch && db_ws > 0 && (!a.dbias_ws || a.dbias_ws_bytes < (size_t)db_ws)) return F8LIN_EWORKSPACE;
   const int64_t mk = a.M * a.K, nk = a.N * a.K, mn = a.M * a.N;
+  const int64_t ld_m = transposed_ld(a.M), ld_n = transposed_ld(a.N);  // row strides of the transposed copies
   const Range outs[11] = {{a.dx, 2 * mk},
                           {a.dw, 2 * nk},
                           {a.dy8, mn},
-                          {a.dy8t, mn},
+                          {a.dy8t, a.N * ld_m},
                           {a.sdy.scale, 8},
                           {a.sdy.amax, dy_given ? 0 : 4},
                           {a.ws, use_ws && !lib_scratch ? (int64_t)kWorkspaceBytes : 0},
@@ -383,7 +391,7 @@ int backward_impl(const f8lin_bwd_args &in, void *stream, bool lib_scratch) {
                           {a.dbias_ws, lib_scratch ? 0 : db_ws},
                           {a.gemm_ws, gemm_ws},
                           {a.dx_amax, a.dx_amax ? 4 : 0}};
-  const Range ins[7] = {{a.dy, 2 * mn},  {a.x8t, mk},     {a.w8t, nk},
+  const Range ins[7] = {{a.dy, 2 * mn},  {a.x8t, a.K * ld_m}, {a.w8t, a.K * ld_n},
                         {a.sx.scale, 8}, {a.sw.scale, 8}, {a.sdy.history, a.mode_dy == F8LIN_DELAYED ? 64 : 0},
                         {a.sdy.amax, dy_given ? 4 : 0}};
   if (any_overlap(outs, 11, ins, 7)) return F8LIN_EINVAL;
@@ -404,6 +412,7 @@ int backward_impl(const f8lin_bwd_args &in, void *stream, bool lib_scratch) {
   }
   uint32_t *ws = (uint32_t *)a.ws;
   CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
+  cdy.ldt = ld_m;
   if (a.dbias) cdy.colsum = a.dbias_ws;  // the cast also sums dY's columns per 128-row tile
   if (a.mode_dy == F8LIN_DYNAMIC && !dy_given) {
     const AmaxTensor t = {a.dy, mn, a.sdy.amax};
@@ -422,6 +431,9 @@ int backward_impl(const f8lin_bwd_args &in, void *stream, bool lib_scratch) {
   GemmDesc g[2] = {{a.dy8, a.w8t, a.sdy.scale + 1, a.sw.scale + 1, a.dx, a.M, a.K, a.N},
                    {a.dy8t, a.x8t, a.sdy.scale + 1, a.sx.scale + 1, a.dw, a.N, a.K, a.M}};
   g[0].amax_out = a.dx_amax;
+  g[0].ldb = ld_n;  // W8^T (K, N)
+  g[1].lda = ld_m;  // dY8^T (N, M)
+  g[1].ldb = ld_m;  // X8^T (K, M)
   F8_TRY(record(a.ev_gemm_begin, s));
   F8_TRY(status_of(launch_gemms(g, 2, F8LIN_E5M2, F8LIN_E4M3, s, a.gemm_ws, (size_t)gemm_ws_use,
                                 use_ws ? ws + kWsQueueOffset : nullptr)));
@@ -437,6 +449,8 @@ using namespace f8lin;
 extern "C" {
 
 size_t f8lin_workspace_bytes(void) { return kWorkspaceBytes; }
+
+int64_t f8lin_transposed_ld(int64_t rows) { return rows < 0 ? 0 : transposed_ld(rows); }
 
 size_t f8lin_dbias_workspace_bytes(int64_t M, int64_t N) {
   if (M < 0 || N < 0) return 0;
@@ -479,7 +493,8 @@ int f8lin_amax(const uint16_t *x, int64_t n, int algo, float *amax_out, void *ws
 int f8lin_cast_transpose(const uint16_t *x, int64_t rows, int64_t cols, int fmt, int mode,
                          const f8lin_state *st, uint8_t *q, uint8_t *qt, void *stream) {
   F8_TRY(validate_cast(x, rows, cols, fmt, mode, st, q, qt));
-  const CastTensor t = {x, rows, cols, st, q, qt};
+  CastTensor t = {x, rows, cols, st, q, qt};
+  t.ldt = transposed_ld(rows);
   return status_of(launch_cast(&t, 1, fmt, mode, (hipStream_t)stream));
 }
 
@@ -507,11 +522,13 @@ int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, 
   Range outs[kMaxGemms], ins[4 * kMaxGemms];
   for (int i = 0; i < count; ++i) {
     const f8lin_gemm_desc &e = d[i];
-    F8_TRY(validate_gemm(e.a, fmt_a, e.b, fmt_b, e.M, e.N, e.K, e.inv_scale_a, e.inv_scale_b, e.c));
+    F8_TRY(validate_gemm(e.a, fmt_a, e.b, fmt_b, e.M, e.N, e.K, e.inv_scale_a, e.inv_scale_b, e.c, e.lda, e.ldb));
     g[i] = GemmDesc{e.a, e.b, e.inv_scale_a, e.inv_scale_b, e.c, e.M, e.N, e.K};
+    g[i].lda = e.lda ? e.lda : e.K;
+    g[i].ldb = e.ldb ? e.ldb : e.K;
     outs[i] = Range{e.c, 2 * e.M * e.N};
-    ins[4 * i] = Range{e.a, e.M * e.K};
-    ins[4 * i + 1] = Range{e.b, e.N * e.K};
+    ins[4 * i] = Range{e.a, e.M * g[i].lda};
+    ins[4 * i + 1] = Range{e.b, e.N * g[i].ldb};
     ins[4 * i + 2] = Range{e.inv_scale_a, 4};
     ins[4 * i + 3] = Range{e.inv_scale_b, 4};
   }

@@ -21,6 +21,8 @@
 //            16 tile rows 16k..16k+15 from LDS, transposes the four 4x4 byte
 //            blocks in registers (v_perm_b32), and writes four 128-bit qt
 //            stores; eight neighbouring threads fill one 128-byte qt segment.
+//            qt's rows are ldt bytes apart (rows, or rows + 128 when rows is
+//            a multiple of 32768: see transposed_ld).
 //   LDS    : 128 rows x 128 bytes, 16-byte chunks XOR-swizzled by
 //            (row / 16) % 8, which makes both the 128-bit row writes and the
 //            4-byte column reads spread over all banks.
@@ -76,6 +78,7 @@ struct CastJob {
   float *amax_acc;        // delayed: where this step's amax accumulates
   float *scale_out;       // {scale, 1/scale}
   uint8_t *q, *qt;
+  int64_t ldt;            // row stride of qt (bytes)
   float *colsum;          // per-tile column sums (bias gradient), or null
   int tiles_x;
   int first;              // first workgroup of this tensor
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const Ca
       }
       if (live && qrow < cols && qcol < rows) {
   #pragma unroll
-        for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4 *>(qt + (qrow + b) * rows + qcol) = out[b];
+        for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4 *>(qt + (qrow + b) * jb.ldt + qcol) = out[b];
       }
     }
     // Bias gradient: this tile's column sums.  The 32 threads of one column
@@ -364,9 +367,10 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
     const CastTensor &t = ts[i];
     const int64_t gx = t.cols > 0 ? (t.cols + kTile - 1) / kTile : 1;
     const int64_t gy = t.rows > 0 ? (t.rows + kTile - 1) / kTile : 1;
-    jobs.j[i] = CastJob{t.x,          t.rows,       t.cols,      t.st->amax, t.partials, t.npartials,
-                        t.st->history, t.st->amax, t.st->scale, t.q,        t.qt,       t.colsum,
-                        (int)gx,       (int)total,  (int)(gx * gy)};
+    jobs.j[i] = CastJob{t.x,          t.rows,       t.cols,      t.st->amax, t.partials,
+                        t.npartials,   t.st->history, t.st->amax, t.st->scale, t.q,
+                        t.qt,          t.ldt ? t.ldt : t.rows,    t.colsum,   (int)gx,
+                        (int)total,    (int)(gx * gy)};
     total += (gx * gy + tpw - 1) / tpw;
   }
   // (An empty tensor may pass a null qt; its workgroup writes no rows.)

@@ -64,6 +64,7 @@
 //     all 2^32 binary32 patterns), staged through LDS per wave and written as
 //     16-byte row segments.
 #include <algorithm>
+#include <vector>
 
 #include "device_common.h"
 #include "internal.h"
@@ -89,6 +90,7 @@ struct Problem {
   uint16_t *c;           // (M, N) bf16; split problems: splits x (M, N) fp32 partial sums
   const uint16_t *bias;  // (N) bf16 or null
   int M, N, K;
+  int lda, ldb;  // row strides (bytes) of A and B, >= K
   int tiles_m, tiles_n;
   int splits;  // split problems: K-block ranges, each a partial product of its own
   float *amax_out;  // AMAX: max |C| (of the rounded bf16 values) folded in here, or null
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     }
     const Problem P = batch.p[pi];
     const int M = P.M, N = P.N;
-    const int ld = P.K;  // row stride of both operands
+    const int lda = P.lda, ldb = P.ldb;  // row strides of the operands
     // the K range this tile contracts: all of K, or its split's whole K blocks
     int K = P.K, kbase = 0, range = 0;
     if constexpr (PARTIAL) {
@@ -261,9 +263,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     // (rows past the tile's last row lie outside the range; bytes past the
     // range's K are masked in issue_one)
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(P.a + (int64_t)m0 * ld + kbase), (short)0, rows_a * ld - kbase, 0x00020000);
+        (void *)(P.a + (int64_t)m0 * lda + kbase), (short)0, rows_a * lda - kbase, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(P.b + (int64_t)n0 * ld + kbase), (short)0, rows_b * ld - kbase, 0x00020000);
+        (void *)(P.b + (int64_t)n0 * ldb + kbase), (short)0, rows_b * ldb - kbase, 0x00020000);
 
     // Global offset (without the K block base) and K byte of each 16-byte
     // slot this lane copies: A slot s = (wave * LA + j) * 64 + lane, same for B.
@@ -272,14 +274,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     for (int j = 0; j < LA; ++j) {
       const int s = (wave * LA + j) * 64 + lane;
       const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-      offa[j] = r * ld + c * 16;
+      offa[j] = r * lda + c * 16;
       kca[j] = c * 16;
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
       const int s = (wave * LB + j) * 64 + lane;
       const int r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-      offb[j] = r * ld + c * 16;
+      offb[j] = r * ldb + c * 16;
       kcb[j] = c * 16;
     }
     // copy q (0 .. LQ-1) of K block kt into stage kt & 1
@@ -550,20 +552,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const Problem P) {
   const int n0 = (int)blockIdx.x * 16;
   const int M = P.M, N = P.N, K = P.K;
   const int rows_b = min(16, N - n0);
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)P.a, (short)0, M * K, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(P.b + (int64_t)n0 * K), (short)0, rows_b * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)P.a, (short)0, M * P.lda, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)(P.b + (int64_t)n0 * P.ldb), (short)0,
+                                                                       rows_b * P.ldb, 0x00020000);
   const int r = lane & 15, kq = (lane >> 4) * 32;
   const int nkb = (K + kBK - 1) / kBK;
   v4f_t acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-  auto load = [&](__amdgpu_buffer_rsrc_t rs, int row, int kb, int k) {
-    // 32 bytes of `row` at K offset k of block kb; chunks past K (or blocks
-    // past the end) point outside the range and read as zeros
+  auto load = [&](__amdgpu_buffer_rsrc_t rs, int ld, int row, int kb, int k) {
+    // 32 bytes of `row` (stride ld) at K offset k of block kb; chunks past K
+    // (or blocks past the end) point outside the range and read as zeros
     const int k0 = kb * kBK + k;
-    const int o0 = (kb < nkb && k0 < K) ? row * K + k0 : kOutOfRange;
-    const int o1 = (kb < nkb && k0 + 16 < K) ? row * K + k0 + 16 : kOutOfRange;
+    const int o0 = (kb < nkb && k0 < K) ? row * ld + k0 : kOutOfRange;
+    const int o1 = (kb < nkb && k0 + 16 < K) ? row * ld + k0 + 16 : kOutOfRange;
     const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o0, 0, 0));
     const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o1, 0, 0));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -572,9 +574,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const Problem P) {
     v8i fb[U], fa[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      fb[u] = load(rsb, r, kb0 + 4 * u, kq);
+      fb[u] = load(rsb, P.ldb, r, kb0 + 4 * u, kq);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) fa[u][m] = load(rsa, m * 16 + r, kb0 + 4 * u, kq);
+      for (int m = 0; m < MT; ++m) fa[u][m] = load(rsa, P.lda, m * 16 + r, kb0 + 4 * u, kq);
     }
     __builtin_amdgcn_sched_barrier(0);  // all U blocks in flight before the first MFMA
 #pragma unroll
@@ -671,6 +673,36 @@ void launch_tiled(const Batch &b, unsigned grid, bool amax, hipStream_t stream) 
     gemm_fp8_tn_kernel<FA, FB, BM, BN, WGM, WGN, MINB, G, false, DYN><<<grid, 64 * WGM * WGN, 0, stream>>>(b);
 }
 
+// Whether the fixed tile stride leaves a batch of big tiles unbalanced: the
+// kernel's walk (each XCD's share of every problem in turn; workgroup j of an
+// XCD's wx takes items j, j + wx, ...) with each tile costing its K blocks
+// plus ~6 blocks of prologue and epilogue, against an even split of the
+// XCD's work.  Balanced batches keep the fixed stride: the work queue's
+// per-tile fetch costs ~4% at 65536 x 4096 x 4096 (dX over 32 K blocks,
+// dW over 512: each workgroup gets 16 of one and 1 of the other either way).
+bool fixed_stride_unbalanced(const Batch &b, int nwg) {
+  constexpr int kTileOverheadBlocks = 6;
+  int64_t worst = 0, total = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const int wx = nwg / kXcds + (x < nwg % kXcds ? 1 : 0);
+    if (wx == 0) continue;
+    std::vector<int64_t> load(wx, 0);
+    int64_t item = 0;
+    for (int i = 0; i < b.count; ++i) {
+      const int T = b.p[i].tiles_m * b.p[i].tiles_n;
+      const int len = T / kXcds + (x < T % kXcds ? 1 : 0);
+      const int64_t cost = (b.p[i].K + kBK - 1) / kBK + kTileOverheadBlocks;
+      for (int t = 0; t < len; ++t, ++item) load[item % wx] += cost;
+    }
+    for (int j = 0; j < wx; ++j) {
+      worst = std::max(worst, load[j] * (int64_t)nwg);
+      total += load[j];
+    }
+  }
+  // worst workgroup more than 3% above the mean
+  return worst * 100 > total * 103;
+}
+
 template <int FA, int FB>
 void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, hipStream_t stream) {
   // skinny problems get their own launches; problems with few long tiles are
@@ -747,7 +779,7 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
     bool amax = false;
     for (int i = 0; i < rest.count; ++i) amax |= rest.p[i].amax_out != nullptr;
-    if (use_big && mixed && queue) {
+    if (use_big && mixed && queue && fixed_stride_unbalanced(rest, std::min(tiles, kCUs))) {
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;
       launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
@@ -806,6 +838,8 @@ hipError_t launch_gemms(const GemmDesc *d, int count, int fmt_a, int fmt_b, hipS
     p.M = (int)d[i].M;
     p.N = (int)d[i].N;
     p.K = (int)d[i].K;
+    p.lda = (int)(d[i].lda ? d[i].lda : d[i].K);
+    p.ldb = (int)(d[i].ldb ? d[i].ldb : d[i].K);
     p.splits = 1;
   }
   if (b.count == 0) return hipSuccess;

@@ -9,6 +9,14 @@
 
 namespace f8lin {
 
+// Row stride (bytes) of the transposed fp8 copy of a tensor with n rows: each
+// of its rows holds n codes.  Strides that are multiples of 32 KB made the
+// GEMMs that contract along such rows ~17% slower (a 4096 x 4096 x 65536
+// product: 975-1032 us at a 65536-byte stride, 818-839 us at 65664), so
+// those get 128 bytes of padding (never read or written).
+constexpr int64_t kTransposeBadStride = 32768, kTransposePad = 128;
+inline int64_t transposed_ld(int64_t n) { return (n > 0 && n % kTransposeBadStride == 0) ? n + kTransposePad : n; }
+
 // Workspace layout (uint32 words): for tensor t of a launch, words
 // [kWsSlotWords*t, +2) hold the atomic variant's running max and ticket;
 // words [kWsPartialsOffset + kMaxGrid*t, +kMaxGrid) the two-pass partials;
@@ -52,6 +60,7 @@ struct CastTensor {
   // if set (e5m2 only): fp32 column sums of x over each 128-row tile,
   // colsum[tile_row * cols + col], for the bias gradient
   float *colsum = nullptr;
+  int64_t ldt = 0;  // row stride of qt in bytes (0: rows)
 };
 // Up to kMaxZero fp32 words the cast launch sets to +0 (from its first
 // workgroup) before anything later on the stream runs: the output-amax words
@@ -86,6 +95,7 @@ struct GemmDesc {
   // if set: max |C| over the rounded bf16 output is folded into *amax_out
   // (atomic max on the fp32 bit pattern; the word must hold +0 or less)
   float *amax_out = nullptr;
+  int64_t lda = 0, ldb = 0;  // row strides of A and B in bytes (0: K)
 };
 // split_ws (optional, 16-byte aligned): room for the fp32 partial products of
 // problems split along K (split_factor > 1); a problem that does not fit

@@ -44,7 +44,7 @@ class State(ctypes.Structure):
 
 class GemmDesc(ctypes.Structure):
     _fields_ = [("a", _vp), ("b", _vp), ("inv_scale_a", _vp), ("inv_scale_b", _vp), ("c", _vp),
-                ("M", _i64), ("N", _i64), ("K", _i64)]
+                ("M", _i64), ("N", _i64), ("K", _i64), ("lda", _i64), ("ldb", _i64)]
 
 
 MAX_BATCH = 4
@@ -67,6 +67,8 @@ class BwdArgs(ctypes.Structure):
                 ("dx_amax", _vp), ("dy_amax_given", _int)]
 
 
+_lib.f8lin_transposed_ld.argtypes = [_i64]
+_lib.f8lin_transposed_ld.restype = _i64
 _lib.f8lin_workspace_bytes.argtypes = []
 _lib.f8lin_workspace_bytes.restype = ctypes.c_size_t
 _lib.f8lin_dbias_workspace_bytes.argtypes = [_i64, _i64]
@@ -117,6 +119,43 @@ def _ptr(t: Optional[torch.Tensor], dtype=None) -> Optional[int]:
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"f8lin: expected {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def transposed_ld(rows: int) -> int:
+    """Row stride (bytes) of the transposed fp8 copy of a tensor with `rows` rows."""
+    return int(_lib.f8lin_transposed_ld(rows))
+
+
+def new_transposed(cols: int, rows: int, device="cuda") -> torch.Tensor:
+    """A (cols, rows) uint8 tensor laid out as the library's transposed copies
+    are: a view into a (cols, transposed_ld(rows)) buffer (uninitialised)."""
+    ld = transposed_ld(rows)
+    buf = torch.empty((cols, ld), dtype=torch.uint8, device=device)
+    return buf[:, :rows] if ld != rows else buf
+
+
+def _ptr_t(t: Optional[torch.Tensor]) -> Optional[int]:
+    """Pointer of a transposed fp8 copy: a (cols, rows) uint8 tensor whose rows
+    are transposed_ld(rows) bytes apart (see new_transposed)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("f8lin: tensors must be on the GPU")
+    if t.dtype != torch.uint8 or t.dim() != 2:
+        raise TypeError("f8lin: a transposed fp8 copy is a 2-D uint8 tensor")
+    if t.numel() > 0 and (t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) != transposed_ld(t.shape[1]))):
+        raise ValueError(f"f8lin: a transposed copy with rows of {t.shape[1]} codes needs a row stride of "
+                         f"{transposed_ld(t.shape[1])} bytes (allocate it with new_transposed)")
+    return t.data_ptr()
+
+
+def _ptr_ld(t: torch.Tensor):
+    """(pointer, row stride) of a 2-D uint8 GEMM operand whose rows are contiguous."""
+    if not t.is_cuda:
+        raise ValueError("f8lin: tensors must be on the GPU")
+    if t.dtype != torch.uint8 or t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+        raise TypeError("f8lin: a GEMM operand is a 2-D uint8 tensor with contiguous rows")
+    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else t.shape[1])
 
 
 def _nbytes(t: Optional[torch.Tensor]) -> int:
@@ -213,8 +252,7 @@ def cast_transpose(x: torch.Tensor, fmt, mode, state: ScalingState, q: torch.Ten
         raise ValueError("cast_transpose takes a 2-D tensor")
     st = state.c_struct()
     _check(_lib.f8lin_cast_transpose(_ptr(x, torch.bfloat16), x.shape[0], x.shape[1], _FMT[fmt], _MODE[mode],
-                                     ctypes.byref(st), _ptr(q, torch.uint8), _ptr(qt, torch.uint8),
-                                     _stream(stream)))
+                                     ctypes.byref(st), _ptr(q, torch.uint8), _ptr_t(qt), _stream(stream)))
 
 
 def cast_f32(v: torch.Tensor, fmt, q: torch.Tensor, stream=None):
@@ -243,8 +281,10 @@ def gemm_batch(items, fmt_a, fmt_b, stream=None):
         N = b.shape[0]
         if b.shape[1] != K or tuple(c.shape) != (M, N):
             raise ValueError("gemm_batch: shape mismatch")
-        arr[i] = GemmDesc(_ptr(a, torch.uint8), _ptr(b, torch.uint8), _ptr(inv_a, torch.float32),
-                          _ptr(inv_b, torch.float32), _ptr(c, torch.bfloat16), M, N, K)
+        pa, lda = _ptr_ld(a)
+        pb, ldb = _ptr_ld(b)
+        arr[i] = GemmDesc(pa, pb, _ptr(inv_a, torch.float32), _ptr(inv_b, torch.float32), _ptr(c, torch.bfloat16),
+                          M, N, K, lda, ldb)
     _check(_lib.f8lin_gemm_batch(arr, len(items), _FMT[fmt_a], _FMT[fmt_b], _stream(stream)))
 
 
@@ -275,7 +315,7 @@ def _fwd_args(x, w, y, x8, x8t, w8, w8t, sx, sw, ws, mode_x, mode_w, algo, bias,
         raise ValueError("forward: bias must have shape (N,)")
     ev0, ev1 = (None, None) if gemm_events is None else gemm_events
     return FwdArgs(M, N, K, _ptr(x, torch.bfloat16), _ptr(w, torch.bfloat16), _ptr(y, torch.bfloat16),
-                   _ptr(x8, torch.uint8), _ptr(x8t, torch.uint8), _ptr(w8, torch.uint8), _ptr(w8t, torch.uint8),
+                   _ptr(x8, torch.uint8), _ptr_t(x8t), _ptr(w8, torch.uint8), _ptr_t(w8t),
                    sx.c_struct(), sw.c_struct(), _MODE[mode_x], _MODE[mode_w], _ALGO[algo], _ptr(ws),
                    _nbytes(ws), None if bias is None else _ptr(bias, torch.bfloat16),
                    1 if w_cast_valid else 0, _event(ev0), _event(ev1), _amax_word(y_amax),
@@ -321,8 +361,8 @@ def backward(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: ScalingState
         raise ValueError("backward: shape mismatch")
     if dbias is not None and tuple(dbias.shape) != (N,):
         raise ValueError("backward: dbias must have shape (N,)")
-    a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr(x8t, torch.uint8), _ptr(w8t, torch.uint8),
-                _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr(dy8t, torch.uint8),
+    a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr_t(x8t), _ptr_t(w8t),
+                _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr_t(dy8t),
                 sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], _ptr(ws),
                 _nbytes(ws), None if dbias is None else _ptr(dbias, torch.bfloat16),
                 None if dbias_ws is None else _ptr(dbias_ws, torch.float32),
@@ -344,8 +384,8 @@ def backward_noalloc(dy, x8t, w8t, dx, dw, dy8, dy8t, sx: ScalingState, sw: Scal
         raise ValueError("backward_noalloc: shape mismatch")
     if dbias is not None and tuple(dbias.shape) != (N,):
         raise ValueError("backward_noalloc: dbias must have shape (N,)")
-    a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr(x8t, torch.uint8), _ptr(w8t, torch.uint8),
-                _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr(dy8t, torch.uint8),
+    a = BwdArgs(M, N, K, _ptr(dy, torch.bfloat16), _ptr_t(x8t), _ptr_t(w8t),
+                _ptr(dx, torch.bfloat16), _ptr(dw, torch.bfloat16), _ptr(dy8, torch.uint8), _ptr_t(dy8t),
                 sx.c_struct(), sw.c_struct(), sdy.c_struct(), _MODE[mode_dy], _ALGO[algo], None, 0,
                 None if dbias is None else _ptr(dbias, torch.bfloat16), None, 0, None, 0,
                 *((None, None) if gemm_events is None else (_event(gemm_events[0]), _event(gemm_events[1]))),
@@ -380,11 +420,11 @@ class LinearBuffers:
         self.dx = torch.empty((M, K), **bf)
         self.dw = torch.empty((N, K), **bf)
         self.x8 = torch.empty((M, K), **u8)
-        self.x8t = torch.empty((K, M), **u8)
+        self.x8t = new_transposed(K, M, device)
         self.w8 = torch.empty((N, K), **u8)
-        self.w8t = torch.empty((K, N), **u8)
+        self.w8t = new_transposed(K, N, device)
         self.dy8 = torch.empty((M, N), **u8)
-        self.dy8t = torch.empty((N, M), **u8)
+        self.dy8t = new_transposed(N, M, device)
         self.sx = ScalingState(device)
         self.sw = ScalingState(device)
         self.sdy = ScalingState(device)

@@ -92,7 +92,7 @@ class _Float8LinearFn(torch.autograd.Function):
         dev = x.device
         u8 = dict(dtype=torch.uint8, device=dev)
         x8 = torch.empty((M, K), **u8)
-        x8t = torch.empty((K, M), **u8)
+        x8t = f8lin.new_transposed(K, M, dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         key = (weight.data_ptr(), weight._version, weight.dtype, str(dev), layer._mode("w"))
         cached = layer._w_cache if (layer.config.reuse_weight_cast and layer._w_cache is not None
@@ -107,7 +107,7 @@ class _Float8LinearFn(torch.autograd.Function):
             # fresh copies: an earlier forward's backward may still read the old ones
             w = weight.to(torch.bfloat16).contiguous()
             w8 = torch.empty((N, K), **u8)
-            w8t = torch.empty((K, N), **u8)
+            w8t = f8lin.new_transposed(K, N, dev)
             mode_w, sw = layer._prepare("w", w)
         f8lin.forward(x, w, y, x8, x8t, w8, w8t, sx, sw, layer.fp8_workspace, mode_x, mode_w,
                       layer.config.amax_algo, bias=b, w_cast_valid=cached is not None)
@@ -131,7 +131,7 @@ class _Float8LinearFn(torch.autograd.Function):
         K = x8t.shape[0]
         dev = dy.device
         dy8 = torch.empty((M, N), dtype=torch.uint8, device=dev)
-        dy8t = torch.empty((N, M), dtype=torch.uint8, device=dev)
+        dy8t = f8lin.new_transposed(N, M, dev)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
         db = db_ws = None

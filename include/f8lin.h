@@ -41,6 +41,11 @@
  *    and multiples of 16 (every row is then a whole number of 16-byte
  *    vectors in both the row-major and the transposed layout).  A zero dimension is allowed and
  *    computes the degenerate result (e.g. dW = 0 when M = 0).
+ *  - A transposed fp8 copy (qt of a (rows, cols) tensor; x8t (K, M), w8t
+ *    (K, N), dy8t (N, M)) has cols rows of f8lin_transposed_ld(rows) bytes:
+ *    the first `rows` bytes of each hold the codes, the rest (128 bytes, only
+ *    when rows is a multiple of 32768) is padding the library never reads
+ *    or writes.  Allocate cols * f8lin_transposed_ld(rows) bytes.
  *  - Arguments are checked before anything is launched; on error nothing is
  *    enqueued and a non-zero f8lin_status is returned.  F8LIN_EHIP reports a
  *    failed launch (hipGetLastError); faults during execution surface at the
@@ -114,6 +119,14 @@ typedef struct {
  * the workspace (every call overwrites them before reading them). */
 size_t f8lin_workspace_bytes(void);
 
+/* Row stride in bytes of the transposed fp8 copy of a tensor with `rows`
+ * rows (each row of the copy holds `rows` codes): rows, or rows + 128 when
+ * rows is a multiple of 32768 (GEMMs contracting along rows whose stride is
+ * a multiple of 32 KB ran ~17% slower on MI355X: 4096 x 4096 x 65536 at a
+ * 65536-byte stride 975-1032 us, at 65664 bytes 818-839 us).  0 for
+ * rows < 0. */
+int64_t f8lin_transposed_ld(int64_t rows);
+
 /* Human-readable name of a status code (static string, never NULL; an
  * unknown code gives "unknown f8lin status"). */
 const char *f8lin_status_str(int status);
@@ -178,13 +191,16 @@ typedef struct {
   const float *inv_scale_a, *inv_scale_b;    /* [1] each */
   uint16_t *c;                               /* (M, N) bf16 output */
   int64_t M, N, K;
+  int64_t lda, ldb; /* row strides of a and b in bytes: 0 (= K), or K <= ld <= 2^22 + 128, a multiple of 16
+                       (e.g. a transposed copy's f8lin_transposed_ld) */
 } f8lin_gemm_desc;
 int f8lin_gemm_batch(const f8lin_gemm_desc *d, int count, int fmt_a, int fmt_b, void *stream);
 
 /* Forward of the layer (pytorch/torchtitan PR #778, "Benchmarking single
  * linear layer forward+backward performance", the forward half):
  * X (M, K) bf16, W (N, K) bf16 -> Y (M, N) bf16.
- * Per tensor: amax (dynamic mode only), then one cast writing both layouts;
+ * Per tensor: amax (dynamic mode only), then one cast writing both layouts
+ * (the transposed ones with the f8lin_transposed_ld row stride);
  * then Y = X8 . W8^T with the dequantisation epilogue.  x8t and w8t (and the
  * scales in sx, sw) are what backward needs; x8 and w8 can be reused or
  * freed after the call.

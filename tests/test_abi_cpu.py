@@ -125,9 +125,21 @@ def test_gemm_rejections(lib):
     assert f(None, 0, B, 0, 32, 48, 64, AMAX, SCALE, C, None) == EINVAL
 
 
+def test_transposed_row_stride(lib):
+    """Transposed copies whose rows hold a multiple of 32768 codes get 128
+    bytes of padding per row; every other length is unpadded."""
+    f = lib.f8lin_transposed_ld
+    f.argtypes = [ctypes.c_int64]
+    f.restype = ctypes.c_int64
+    for n, want in ((0, 0), (16, 16), (4096, 4096), (16384, 16384), (32752, 32752), (32768, 32896),
+                    (65536, 65664), (98304, 98432), (1 << 22, (1 << 22) + 128), (-16, 0)):
+        assert f(n) == want, n
+
+
 class GemmDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("a", "b", "inv_scale_a", "inv_scale_b", "c")] + \
-               [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+               [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("lda", ctypes.c_int64),
+                ("ldb", ctypes.c_int64)]
 
 
 def test_gemm_batch_rejections(lib):
@@ -151,6 +163,13 @@ def test_gemm_batch_rejections(lib):
     assert f(bad, 2, 0, 0, None) == EINVAL                      # the two outputs overlap
     bad = (GemmDesc * 2)(ok0, GemmDesc(B, C, AMAX, SCALE, C2, 48, 32, 64))
     assert f(bad, 2, 0, 0, None) == EINVAL                      # second input is the first output
+    # row strides: 0 means K; otherwise at least K and a multiple of 16, and the overlap checks use them
+    assert f((GemmDesc * 1)(GemmDesc(A, B, AMAX, SCALE, C, 32, 48, 64, 48, 0)), 1, 0, 0, None) == ESHAPE  # lda < K
+    assert f((GemmDesc * 1)(GemmDesc(A, B, AMAX, SCALE, C, 32, 48, 64, 0, 72)), 1, 0, 0, None) == ESHAPE  # not x16
+    assert f((GemmDesc * 1)(GemmDesc(A, B, AMAX, SCALE, A + 32 * 64 - 16, 32, 48, 64, 0, 0)), 1, 0, 0, None) == EINVAL
+    # a strided A reaches further: C right after A's unstrided bytes now overlaps it
+    assert f((GemmDesc * 1)(GemmDesc(A, B, AMAX, SCALE, A + 32 * 64 + 4096, 32, 48, 64, 256, 0)), 1, 0, 0,
+             None) == EINVAL
 
 
 class Fwd(ctypes.Structure):

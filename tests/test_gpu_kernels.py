@@ -118,7 +118,7 @@ def _cast_gpu(f8, x_dev, fmt, mode="dynamic", state=None, amax_value=None, trans
     if amax_value is not None:
         st.amax.fill_(float(amax_value))
     q = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
-    qt = torch.empty((cols, rows), dtype=torch.uint8, device=DEV) if transpose else None
+    qt = f8.new_transposed(cols, rows, DEV) if transpose else None
     f8.cast_transpose(x_dev, fmt, mode, st, q, qt)
     torch.cuda.synchronize()
     return st, q, qt
@@ -288,3 +288,40 @@ def test_gemm_k_zero_gives_zeros(f8):
     f8.gemm(torch.from_numpy(a).to(DEV), 0, torch.from_numpy(b).to(DEV), 0, ia, ia, c)
     torch.cuda.synchronize()
     assert torch.count_nonzero(c).item() == 0
+
+
+def test_transposed_copy_padding_is_never_touched(f8):
+    """A tensor with 32768 rows: its transposed copy's rows are 32768 + 128
+    bytes apart.  The cast writes the codes (equal to the oracle's transpose)
+    and leaves every padding byte as it was; a GEMM reading that copy as its
+    operand (row stride from the tensor) agrees with one reading a
+    contiguous copy of the same codes, bit for bit."""
+    rows, cols = 32768, 256
+    ld = f8.transposed_ld(rows)
+    assert ld == rows + 128 and f8.transposed_ld(16384) == 16384 and f8.transposed_ld(98304) == 98304 + 128
+    x = inputs.random_bf16((rows, cols), seed=91)
+    raw = torch.full((cols, ld), 0xA5, dtype=torch.uint8, device=DEV)
+    qt = raw[:, :rows]
+    st = f8.ScalingState(DEV)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    ws = f8.new_workspace(DEV)
+    f8.amax(x.to(DEV), st.amax, ws, "atomic")
+    f8.cast_transpose(x.to(DEV), "e4m3", "dynamic", st, q, qt)
+    torch.cuda.synchronize()
+    assert torch.all(raw[:, rows:] == 0xA5).item(), "padding written"
+    s, _ = oracle.scale(oracle.amax(bits(x)), oracle.E4M3)
+    rq, rqt, _ = oracle.cast(bits(x), oracle.E4M3, s)
+    assert np.array_equal(u8(qt), rqt) and np.array_equal(u8(q), rq)
+    # the padded copy as both operands of a GEMM contracting over its 32768 columns
+    c_pad = torch.empty((cols, cols), dtype=torch.bfloat16, device=DEV)
+    c_ref = torch.empty((cols, cols), dtype=torch.bfloat16, device=DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    qtc = qt.contiguous()
+    f8.gemm_batch([(qt, qt, one, one, c_pad)], "e4m3", "e4m3")
+    f8.gemm(qtc, "e4m3", qtc, "e4m3", one, one, c_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(c_pad.view(torch.int16), c_ref.view(torch.int16))
+    gemm_check(bf16_to_f64(c_pad), oracle.gemm_ref(rqt, oracle.E4M3, rqt, oracle.E4M3, 1.0, 1.0), what="padded operand")
+    # a contiguous tensor with such rows is refused by the binding (it is not the library's layout)
+    with pytest.raises(ValueError):
+        f8.cast_transpose(x.to(DEV), "e4m3", "dynamic", st, q, torch.empty((cols, rows), dtype=torch.uint8, device=DEV))

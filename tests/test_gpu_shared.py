@@ -27,7 +27,7 @@ def _lin(f8, M, N, K, seed, bias=False):
     w = inputs.random_bf16((N, K), seed=seed, std=K ** -0.5).to(DEV)
     d = {"w": w, "y": torch.empty((M, N), dtype=torch.bfloat16, device=DEV),
          "w8": torch.empty((N, K), dtype=torch.uint8, device=DEV),
-         "w8t": torch.empty((K, N), dtype=torch.uint8, device=DEV), "sw": f8.ScalingState(DEV)}
+         "w8t": f8.new_transposed(K, N, DEV), "sw": f8.ScalingState(DEV)}
     if bias:
         d["bias"] = inputs.random_bf16((N,), seed=seed + 1, std=0.1).to(DEV)
     return d
@@ -46,14 +46,14 @@ def test_shared_x_equals_separate_forwards(f8, shape, algo):
     x = inputs.random_bf16((M, K), seed=M + K).to(DEV)
     lins = [_lin(f8, M, N, K, seed=10 + i, bias=(i == 1)) for i, N in enumerate(Ns)]
     x8 = torch.empty((M, K), dtype=torch.uint8, device=DEV)
-    x8t = torch.empty((K, M), dtype=torch.uint8, device=DEV)
+    x8t = f8.new_transposed(K, M, DEV)
     sx = f8.ScalingState(DEV)
     ws = f8.new_workspace(DEV)
     f8.forward_shared_x(x, x8, x8t, sx, ws, lins, "dynamic", algo)
     torch.cuda.synchronize()
     for i, l in enumerate(lins):
         ref = _lin(f8, M, l["w"].shape[0], K, seed=10 + i, bias=(i == 1))
-        rx8, rx8t, rsx, rws = torch.empty_like(x8), torch.empty_like(x8t), f8.ScalingState(DEV), f8.new_workspace(DEV)
+        rx8, rx8t, rsx, rws = torch.empty_like(x8), f8.new_transposed(K, M, DEV), f8.ScalingState(DEV), f8.new_workspace(DEV)
         f8.forward(x, ref["w"], ref["y"], rx8, rx8t, ref["w8"], ref["w8t"], rsx, ref["sw"], rws, "dynamic", "dynamic",
                    algo, bias=ref.get("bias"))
         torch.cuda.synchronize()
@@ -99,7 +99,7 @@ def test_shared_x_mixed_modes_and_reuse(f8):
     b["mode_w"] = "delayed"
     # c's cast comes from an earlier forward of the same weight
     x8 = torch.empty((M, K), dtype=torch.uint8, device=DEV)
-    x8t = torch.empty((K, M), dtype=torch.uint8, device=DEV)
+    x8t = f8.new_transposed(K, M, DEV)
     sx, ws = f8.ScalingState(DEV), f8.new_workspace(DEV)
     f8.forward(x, c["w"], c["y"], x8, x8t, c["w8"], c["w8t"], sx, c["sw"], ws)
     c["w_cast_valid"] = True
@@ -111,7 +111,7 @@ def test_shared_x_mixed_modes_and_reuse(f8):
         ref["w"] = l["w"]
         if l.get("mode_w") == "delayed":
             ref["sw"].history.fill_(0.25)
-        rx8, rx8t = torch.empty_like(x8), torch.empty_like(x8t)
+        rx8, rx8t = torch.empty_like(x8), f8.new_transposed(K, M, DEV)
         f8.forward(x, l["w"], ref["y"], rx8, rx8t, ref["w8"], ref["w8t"], f8.ScalingState(DEV), ref["sw"],
                    f8.new_workspace(DEV), "dynamic", l.get("mode_w", "dynamic"))
         torch.cuda.synchronize()
