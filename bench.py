@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--only-timed", action="store_true", help="skip everything after the headline (for profiling)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes three times (counter calibration)")
+    p.add_argument("--ceilings", action="store_true",
+                   help="only measure this GPU's ceilings: HBM streaming (own read / write / copy kernels), "
+                        "MFMA issue from registers with its clock, and the GEMM's own K loop at long K")
     return p.parse_args()
 
 
@@ -112,6 +115,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}), flush=True)
+        return
+
+    if args.ceilings:
+        print(json.dumps(ceilings(torch, f8lin)), flush=True)
         return
 
     wl = inputs.WORKLOADS[args.workload]
@@ -296,6 +303,132 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, wl, sets, np, torch)
     print(json.dumps(out), flush=True)
+
+
+def ceilings(torch, f8lin):
+    """The chip's ceilings for the path's two bounds, from kernels shaped like
+    the path's own (libf8lin_probe.so), each after a settle and timed with HIP
+    events: (1) HBM streaming with 128-bit accesses over 1 GiB (larger than the
+    256 MB last-level cache), read only, write only and copy, over a few grid
+    shapes (the best is the ceiling); (2) fp8 MFMA issue from registers, eight
+    waves per CU, with the shader clock each workgroup read; (3) the product
+    GEMM at one tile per CU and a long contraction (4096 x 4096 x 65408 and x
+    16384), where its K loop is nearly all of the launch."""
+    import ctypes
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = torch.cuda.current_stream()
+    lib = ctypes.CDLL(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "libf8lin_probe.so"))
+    lib.f8probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.f8probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+
+    def timed(fn, reps):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+    out = {"what": "ceilings of this GPU, measured by bench.py --ceilings"}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    red = torch.zeros(4096, dtype=torch.int32, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:  # settle
+        assert lib.f8probe_stream(2, src.data_ptr(), dst.data_ptr(), nbytes, 1024, 256, None, s.cuda_stream) == 0
+        torch.cuda.synchronize()
+    shapes = [(256, 512), (512, 512), (1024, 256), (2048, 256), (4096, 256)]
+    stream_res = {}
+    for mode, name, moved in ((0, "read", 1), (1, "write", 1), (2, "copy", 2)):
+        best = None
+        per = {}
+        for grid, block in shapes:
+            def fn():
+                r = lib.f8probe_stream(mode, src.data_ptr(), dst.data_ptr(), nbytes, grid, block,
+                                       red.data_ptr(), s.cuda_stream)
+                assert r == 0, r
+            us = timed(fn, 10)
+            gbs = moved * nbytes / (us * 1e-6) / 1e9
+            per[f"{grid}x{block}"] = round(gbs, 1)
+            best = gbs if best is None else max(best, gbs)
+        stream_res[name] = {"best_gbs": round(best, 1), "frac_hbm_peak": round(best / PEAK_HBM_GBS, 4),
+                            "by_grid": per}
+    out["hbm_stream_1gib"] = stream_res
+    del src, dst
+    torch.cuda.empty_cache()
+    # smaller tensors, as the layer workloads have them: cold data (a pool of
+    # buffers larger than the last-level cache, rotated), one launch at a time
+    # between HIP events, read and copy with the best grid shape above
+    by_size = {}
+    for mib in (16, 32, 64, 128, 256):
+        nb = mib << 20
+        pool = max(4, (1 << 30) // nb)
+        srcs = torch.ones(pool * nb, dtype=torch.uint8, device=dev).view(pool, nb)
+        dsts = torch.empty(pool * nb, dtype=torch.uint8, device=dev).view(pool, nb)
+        row = {}
+        for mode, name, moved in ((0, "read", 1), (2, "copy", 2)):
+            evs = []
+            for rep in range(3 * pool):
+                i = rep % pool
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                assert lib.f8probe_stream(mode, srcs[i].data_ptr(), dsts[i].data_ptr(), nb, 256, 512,
+                                          red.data_ptr(), s.cuda_stream) == 0
+                e1.record(s)
+                if rep >= pool:
+                    evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / len(evs)
+            row[name] = {"us": round(us, 2), "gbs": round(moved * nb / (us * 1e-6) / 1e9, 1)}
+        by_size[f"{mib}MiB"] = row
+        del srcs, dsts
+        torch.cuda.empty_cache()
+    out["hbm_stream_by_size_cold"] = by_size
+
+    grid, iters = 256, 5000
+    sink = torch.empty(grid * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+
+    def mf():
+        assert lib.f8probe_mfma(grid, iters, sink.data_ptr(), clocks.data_ptr(), s.cuda_stream) == 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        mf()
+        torch.cuda.synchronize()
+    us = timed(mf, 10)
+    flops = grid * 8 * iters * 8 * 131072
+    c = clocks.view(grid, 2).cpu().double()
+    ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1  # cycles per 100 MHz tick
+    out["mfma_f8_from_registers"] = {"tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                                     "frac_fp8_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                     "shader_clock_ghz": round(ghz, 3), "us_per_launch": round(us, 1),
+                                     "what": "256 workgroups x 8 waves, 8 independent 32x32x64 MFMA chains per wave"}
+    # the GEMM's own K loop: one 256 x 256 tile per CU, long contraction
+    loop = {}
+    for K in (65408, 16384):
+        a = torch.randint(0, 0x70, (4096 * K,), dtype=torch.uint8, device=dev).view(4096, K)
+        b = torch.randint(0, 0x70, (4096 * K,), dtype=torch.uint8, device=dev).view(4096, K)
+        cc = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+        one = torch.ones(1, dtype=torch.float32, device=dev)
+
+        def g():
+            f8lin.gemm(a, "e5m2", b, "e4m3", one, one, cc)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            g()
+            torch.cuda.synchronize()
+        us = timed(g, 5)
+        loop[f"4096x4096x{K}"] = {"us": round(us, 1), "tflops": round(2 * 4096 * 4096 * K / (us * 1e-6) / 1e12, 1)}
+        del a, b, cc
+    out["gemm_k_loop"] = loop
+    return out
 
 
 def copy_reference(torch, stream, nbytes=1 << 30, reps=20):

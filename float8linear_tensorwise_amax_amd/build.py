@@ -1,8 +1,9 @@
 """Builds libf8lin.so (the HIP kernels + C ABI) in-tree, for gfx950 only.
 
 Each csrc/*.hip is compiled by hipcc in parallel, then linked into one shared
-library next to this file.  All device code is built with packed-fp32
-instruction generation turned off.
+library next to this file.  The ceiling probes (csrc/probe/*.hip, measurement
+tooling that `bench.py --ceilings` drives) go into libf8lin_probe.so.  All
+device code is built with packed-fp32 instruction generation turned off.
 """
 import os
 import subprocess
@@ -13,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libf8lin.so")
+PROBE_LIB = os.path.join(HERE, "libf8lin_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,8 +25,8 @@ COMMON = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d=CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
@@ -43,17 +45,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    probe_srcs = sources(os.path.join(CSRC, "probe"))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
     return LIB
 
 
