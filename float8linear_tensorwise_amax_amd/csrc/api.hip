@@ -262,14 +262,21 @@ int forward_impl(const f8lin_fwd_args *list, int count, void *stream) {
     const int n = (i + 1 < nt && modes[i + 1] == modes[i]) ? 2 : 1;
     CastTensor pair[2] = {ct[i], n > 1 ? ct[i + 1] : ct[i]};
     if (modes[i] == F8LIN_DYNAMIC) {
-      // amax passes for the tensors whose amax is not handed in
+      // amax passes for the tensors whose amax is not handed in; when all of
+      // them are small, the cast computes them itself (no amax launch)
       AmaxTensor am[2];
       int slot[2], na = 0;
+      bool all_small = true;
       for (int j = 0; j < n; ++j)
         if (!given[i + j]) {
           slot[na] = j;
           am[na++] = AmaxTensor{pair[j].x, pair[j].rows * pair[j].cols, pair[j].st->amax};
+          all_small = all_small && pair[j].rows * pair[j].cols <= kSelfAmaxElems;
         }
+      if (na > 0 && all_small) {
+        for (int j = 0; j < na; ++j) pair[slot[j]].self_amax = 1;
+        na = 0;
+      }
       if (na > 0 && a0.algo == F8LIN_AMAX_TWOPASS) {
         const uint32_t *parts[2] = {nullptr, nullptr};
         int nparts[2] = {0, 0};
@@ -414,7 +421,9 @@ int backward_impl(const f8lin_bwd_args &in, void *stream, bool lib_scratch) {
   CastTensor cdy = {a.dy, a.M, a.N, &a.sdy, a.dy8, a.dy8t};
   cdy.ldt = ld_m;
   if (a.dbias) cdy.colsum = a.dbias_ws;  // the cast also sums dY's columns per 128-row tile
-  if (a.mode_dy == F8LIN_DYNAMIC && !dy_given) {
+  if (a.mode_dy == F8LIN_DYNAMIC && !dy_given && mn <= kSelfAmaxElems) {
+    cdy.self_amax = 1;  // small dY: the cast computes its amax itself
+  } else if (a.mode_dy == F8LIN_DYNAMIC && !dy_given) {
     const AmaxTensor t = {a.dy, mn, a.sdy.amax};
     if (a.algo == F8LIN_AMAX_TWOPASS)
       F8_TRY(status_of(launch_amax_partials(&t, 1, ws, &cdy.partials, &cdy.npartials, s)));

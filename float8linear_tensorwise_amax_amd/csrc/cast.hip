@@ -74,6 +74,7 @@ struct CastJob {
   float *amax;            // dynamic: this tensor's amax (written here when partials are given)
   const uint32_t *partials;  // dynamic, two-pass: the partial magnitude maxima, or null
   int npartials;
+  int self_amax;          // dynamic, small tensor: every workgroup reduces the whole tensor itself
   const float *history;   // delayed: its amax history
   float *amax_acc;        // delayed: where this step's amax accumulates
   float *scale_out;       // {scale, 1/scale}
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const Ca
   if constexpr (MODE == F8LIN_DYNAMIC) {
     if (jb.partials) {
       pmag = t < jb.npartials ? jb.partials[t] : 0u;  // at most kMaxGrid <= kThreads partials
-    } else {
+    } else if (!jb.self_amax) {
       a = jb.amax[0];
     }
   } else {
@@ -266,10 +267,33 @@ __global__ __launch_bounds__(kThreads * TPW) void cast_transpose_kernel(const Ca
 
   u32x4 in[4][2];
   load(in);
+  if constexpr (MODE == F8LIN_DYNAMIC) {
+    if (jb.self_amax) {
+      // A small tensor (at most kSelfAmaxElems elements, whole 8-element
+      // vectors since cols is a multiple of 16): every workgroup reads all of
+      // it -- from the L2 once the first has -- instead of a separate amax
+      // launch; the same 15-bit magnitude max, so the same bits.
+      const u32x4 *__restrict__ xv = reinterpret_cast<const u32x4 *>(x);
+      const int nv = (int)(rows * cols / 8);
+      int i = t;
+      for (; i + 7 * kThreads < nv; i += 8 * kThreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = xv[i + u * kThreads];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          pmag = mag_max2(mag_max2(mag_max2(mag_max2(pmag, v[u].x), v[u].y), v[u].z), v[u].w);
+      }
+      for (; i < nv; i += kThreads) {
+        const u32x4 v = xv[i];
+        pmag = mag_max2(mag_max2(mag_max2(mag_max2(pmag, v.x), v.y), v.z), v.w);
+      }
+    }
+  }
 
   // The scale.
   if constexpr (MODE == F8LIN_DYNAMIC) {
-    if (jb.partials) {
+    if (jb.partials || jb.self_amax) {
       uint32_t m = pmag;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
@@ -367,10 +391,10 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
     const CastTensor &t = ts[i];
     const int64_t gx = t.cols > 0 ? (t.cols + kTile - 1) / kTile : 1;
     const int64_t gy = t.rows > 0 ? (t.rows + kTile - 1) / kTile : 1;
-    jobs.j[i] = CastJob{t.x,          t.rows,       t.cols,      t.st->amax, t.partials,
-                        t.npartials,   t.st->history, t.st->amax, t.st->scale, t.q,
-                        t.qt,          t.ldt ? t.ldt : t.rows,    t.colsum,   (int)gx,
-                        (int)total,    (int)(gx * gy)};
+    jobs.j[i] = CastJob{t.x,           t.rows,       t.cols,      t.st->amax,  t.partials,
+                        t.npartials,   t.self_amax,  t.st->history, t.st->amax, t.st->scale,
+                        t.q,           t.qt,         t.ldt ? t.ldt : t.rows,    t.colsum,
+                        (int)gx,       (int)total,   (int)(gx * gy)};
     total += (gx * gy + tpw - 1) / tpw;
   }
   // (An empty tensor may pass a null qt; its workgroup writes no rows.)

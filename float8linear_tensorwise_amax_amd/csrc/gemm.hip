@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   // in the same array (a second __shared__ object makes the compiler wait
   // for the LDS copies before every fragment read)
   constexpr int kDynBytes = DYN ? 16 : 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB + kDynBytes + (AMAX ? 4 * NW : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB + kDynBytes + (AMAX ? 4 * 64 * NW : 0)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;  // K half within a 64-byte sub-step
@@ -191,26 +191,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   // wait for block 0 does, so its use there costs no wait of its own.
   int *const next_item = reinterpret_cast<int *>(smem + 2 * STB);
   int par = 0;
-  // AMAX: each wave's running max magnitude (15-bit bf16 field) of the
-  // values problem amax_pi's tiles stored, in LDS (red[wave], kept by lane
-  // 0: no register lives across the K loop for it); flushed by a workgroup
-  // max and one atomic.
+  // AMAX: each lane's running max magnitude (15-bit bf16 field) of the
+  // values problem amax_pi's tiles stored, in LDS (red[tid], updated by its
+  // own lane after the tile's stores are issued: no register lives across the
+  // K loop for it, and no cross-lane step runs per tile); flushed by a
+  // workgroup max and one atomic.
   uint32_t *const red = reinterpret_cast<uint32_t *>(smem + 2 * STB + kDynBytes);
   int amax_pi = -1;
-  if constexpr (AMAX) {
-    if (lane == 0) red[wave] = 0;  // ordered before its first use by the first tile's barriers
-  }
+  if constexpr (AMAX) red[tid] = 0;  // only this lane touches red[tid] until a flush
   auto flush_amax = [&]() {
     if constexpr (AMAX) {
-      __syncthreads();  // every wave's last update of red is in
+      uint32_t m = red[tid];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+      __syncthreads();  // every lane has read its word
+      if (lane == 0) red[wave] = m;
+      __syncthreads();
       if (tid == 0 && amax_pi >= 0 && batch.p[amax_pi].amax_out) {
-        uint32_t m = red[0];
 #pragma unroll
         for (int w = 1; w < NW; ++w) m = max(m, red[w]);
         atomicMax(reinterpret_cast<uint32_t *>(batch.p[amax_pi].amax_out), m << 16);
       }
-      __syncthreads();  // read before any wave clears its word
-      if (lane == 0) red[wave] = 0;
+      __syncthreads();  // read before any lane clears its word
+      red[tid] = 0;
     }
   };
   uint32_t *const queue = DYN ? batch.queue + xcd * kQueueWords : nullptr;
@@ -501,11 +504,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
           omag = mag_max2(mag_max2(mag_max2(mag_max2(omag, vals[k].x), vals[k].y), vals[k].z), vals[k].w);
       }
     }
-    if constexpr (AMAX) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) omag = max(omag, (uint32_t)__shfl_xor((int)omag, off, 64));
-      if (lane == 0) red[wave] = max(red[wave], omag);
-    }
     if (batch.nt_stores) {
 #pragma unroll
       for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 2);  // nt
@@ -513,6 +511,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
 #pragma unroll
       for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 0);
     }
+    if constexpr (AMAX) red[tid] = max(red[tid], omag);  // after the stores are issued
     __syncthreads();  // staging reads done before the next tile's copies land
     if constexpr (DYN) {
       it = __builtin_amdgcn_readfirstlane(next_item[par]);

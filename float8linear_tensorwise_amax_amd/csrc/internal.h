@@ -57,6 +57,9 @@ struct CastTensor {
   // st->amax is written), or null to read st->amax
   const uint32_t *partials = nullptr;
   int npartials = 0;
+  // dynamic mode, at most kSelfAmaxElems elements: the cast computes the
+  // amax itself (every workgroup over the whole tensor; st->amax is written)
+  int self_amax = 0;
   // if set (e5m2 only): fp32 column sums of x over each 128-row tile,
   // colsum[tile_row * cols + col], for the bias gradient
   float *colsum = nullptr;
@@ -77,6 +80,11 @@ hipError_t launch_cast(const CastTensor *ts, int count, int fmt, int mode, hipSt
 // summed in order of t.
 hipError_t launch_dbias(const float *colsum, int64_t tiles, int64_t n_cols, uint16_t *db, hipStream_t stream);
 constexpr int kCastTile = 128;
+// Tensors this small (128 Ki elements, 256 KB) have their amax computed inside
+// the cast launch instead of by an amax launch of their own: at 16 x 4096 the
+// separate launch cost ~3.5 us, more than every workgroup reading the whole
+// 128 KB tensor from the L2.
+constexpr int64_t kSelfAmaxElems = 128 * 1024;
 
 hipError_t launch_cast_f32(const float *v, int64_t n, int fmt, uint8_t *q, hipStream_t stream);
 

@@ -325,3 +325,43 @@ def test_transposed_copy_padding_is_never_touched(f8):
     # a contiguous tensor with such rows is refused by the binding (it is not the library's layout)
     with pytest.raises(ValueError):
         f8.cast_transpose(x.to(DEV), "e4m3", "dynamic", st, q, torch.empty((cols, rows), dtype=torch.uint8, device=DEV))
+
+
+@pytest.mark.parametrize("algo", ["atomic", "twopass"])
+@pytest.mark.parametrize("shape", [(16, 4096), (128, 1024), (32, 4112), (48, 160), (0, 64)])
+def test_small_tensor_cast_computes_its_own_amax(f8, algo, shape):
+    """Tensors of at most 128 Ki elements have their amax computed inside the
+    cast launch (every workgroup reduces the whole tensor).  Through the
+    forward and backward, amax, scale and bytes equal the oracle's bit for bit,
+    with special values planted (the maximum in the last element, subnormals,
+    -0), at the threshold (128 x 1024) and just above it (32 x 4112, which
+    takes the amax launch), and with NaN / Inf (NaN amax, NaN scale)."""
+    M, K = shape
+    N = 64
+    for variant in ("plain", "max_last", "nan", "inf"):
+        x = inputs.random_bf16((M, K), seed=M + K + 1)
+        if M * K:
+            flat = x.view(-1)
+            flat[1] = -0.0
+            flat[2] = float.fromhex("0x1p-130")  # bf16 subnormal
+            if variant == "max_last":
+                flat[-1] = -1000.0
+            elif variant == "nan":
+                flat[M * K // 2] = float("nan")
+            elif variant == "inf":
+                flat[3] = float("-inf")
+        w = inputs.random_bf16((N, K), seed=7, std=K ** -0.5)
+        dy = inputs.random_bf16((M, N), seed=8, std=0.03)
+        buf = f8.LinearBuffers(M, N, K, DEV)
+        buf.forward(x.to(DEV), w.to(DEV), "dynamic", algo)
+        buf.backward(dy.to(DEV), "dynamic", algo)
+        torch.cuda.synchronize()
+        for st, t, fmt, q, qt in ((buf.sx, x, oracle.E4M3, buf.x8, buf.x8t), (buf.sdy, dy, oracle.E5M2, buf.dy8, buf.dy8t)):
+            a = oracle.amax(bits(t))
+            assert f32_bits(st.amax)[0] == np_f32_bits(a), (variant, shape)
+            s, inv = oracle.scale(a, fmt)
+            assert f32_bits(st.scale)[0] == np_f32_bits(s), (variant, shape)
+            if variant != "nan":  # a NaN scale makes every code a NaN code: which one is not part of the contract
+                rq, rqt, _ = oracle.cast(bits(t), fmt, s)
+                assert np.array_equal(u8(q), rq) and np.array_equal(u8(qt), rqt), (variant, shape)
+        del buf
