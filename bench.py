@@ -311,9 +311,12 @@ def ceilings(torch, f8lin):
     events: (1) HBM streaming with 128-bit accesses over 1 GiB (larger than the
     256 MB last-level cache), read only, write only and copy, over a few grid
     shapes (the best is the ceiling); (2) fp8 MFMA issue from registers, eight
-    waves per CU, with the shader clock each workgroup read; (3) the product
-    GEMM at one tile per CU and a long contraction (4096 x 4096 x 65408 and x
-    16384), where its K loop is nearly all of the launch."""
+    waves per CU, with the shader clock each workgroup read, on constant and on
+    random operands, and the same MFMAs fed from LDS as the GEMM's K loop feeds
+    them (without its global copies); (3) the product GEMM at one tile per CU
+    and a long contraction (4096 x 4096 x 65408 and x 16384), where its K loop
+    is nearly all of the launch.  Random operand codes are finite, of either
+    sign and every exponent."""
     import ctypes
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -321,7 +324,9 @@ def ceilings(torch, f8lin):
     lib = ctypes.CDLL(os.path.join(ROOT, "float8linear_tensorwise_amax_amd", "libf8lin_probe.so"))
     lib.f8probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.f8probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.f8probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    lib.f8probe_mfma_lds.argtypes = lib.f8probe_mfma.argtypes
 
     def timed(fn, reps):
         fn()
@@ -392,29 +397,51 @@ def ceilings(torch, f8lin):
         torch.cuda.empty_cache()
     out["hbm_stream_by_size_cold"] = by_size
 
+    def codes(n, fmt):
+        # finite codes of either sign, every exponent (e4m3: 0x7F is NaN;
+        # e5m2: 0x7C-0x7F are Inf and NaN), as scaled real data has them
+        top = 0x7F if fmt == "e4m3" else 0x7C
+        mag = torch.randint(0, top, (n,), dtype=torch.uint8, device=dev)
+        return mag | (torch.randint(0, 2, (n,), dtype=torch.uint8, device=dev) << 7)
+
     grid, iters = 256, 5000
     sink = torch.empty(grid * 512, dtype=torch.float32, device=dev)
     clocks = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+    ops = codes(grid * 512 * 48 * 4, "e4m3")
+    lds_src = codes(131072, "e4m3")
 
-    def mf():
-        assert lib.f8probe_mfma(grid, iters, sink.data_ptr(), clocks.data_ptr(), s.cuda_stream) == 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.5:
-        mf()
-        torch.cuda.synchronize()
-    us = timed(mf, 10)
-    flops = grid * 8 * iters * 8 * 131072
-    c = clocks.view(grid, 2).cpu().double()
-    ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1  # cycles per 100 MHz tick
-    out["mfma_f8_from_registers"] = {"tflops": round(flops / (us * 1e-6) / 1e12, 1),
-                                     "frac_fp8_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
-                                     "shader_clock_ghz": round(ghz, 3), "us_per_launch": round(us, 1),
-                                     "what": "256 workgroups x 8 waves, 8 independent 32x32x64 MFMA chains per wave"}
+    def mfma_run(fn, flops, what):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            fn()
+            torch.cuda.synchronize()
+        us = timed(fn, 10)
+        c = clocks.view(grid, 2).cpu().double()
+        ghz = float((c[:, 0] / c[:, 1]).mean()) * 0.1  # cycles per 100 MHz tick
+        tf = flops / (us * 1e-6) / 1e12
+        return {"tflops": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                "shader_clock_ghz": round(ghz, 3), "us_per_launch": round(us, 1), "what": what}
+
+    reg_flops = grid * 8 * iters * 8 * 131072
+    out["mfma_f8_from_registers"] = mfma_run(
+        lambda: lib.f8probe_mfma(grid, iters, None, sink.data_ptr(), clocks.data_ptr(), s.cuda_stream),
+        reg_flops, "256 workgroups x 8 waves, 8 independent 32x32x64 MFMA chains per wave, small constant operands")
+    out["mfma_f8_from_registers_random"] = mfma_run(
+        lambda: lib.f8probe_mfma(grid, iters, ops.data_ptr(), sink.data_ptr(), clocks.data_ptr(), s.cuda_stream),
+        reg_flops, "the same, operands random finite e4m3 codes of either sign")
+    lds_iters = iters // 2
+    out["mfma_f8_from_lds"] = mfma_run(
+        lambda: lib.f8probe_mfma_lds(grid, lds_iters, lds_src.data_ptr(), sink.data_ptr(), clocks.data_ptr(),
+                                     s.cuda_stream),
+        grid * 8 * lds_iters * 16 * 131072,
+        "the GEMM's K loop without its global copies: 128 x 64 wave tiles, fragments read from two 64 KB LDS stages "
+        "of random codes, one barrier per 128-byte K block")
+    del ops, lds_src
     # the GEMM's own K loop: one 256 x 256 tile per CU, long contraction
     loop = {}
     for K in (65408, 16384):
-        a = torch.randint(0, 0x70, (4096 * K,), dtype=torch.uint8, device=dev).view(4096, K)
-        b = torch.randint(0, 0x70, (4096 * K,), dtype=torch.uint8, device=dev).view(4096, K)
+        a = codes(4096 * K, "e5m2").view(4096, K)
+        b = codes(4096 * K, "e4m3").view(4096, K)
         cc = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
         one = torch.ones(1, dtype=torch.float32, device=dev)
 

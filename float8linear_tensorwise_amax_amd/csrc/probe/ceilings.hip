@@ -14,7 +14,17 @@
 //     the GEMM), two waves per SIMD, one workgroup of eight waves per CU; each
 //     workgroup records s_memtime (shader clock) and s_memrealtime (a
 //     constant 100 MHz) around its loop, so the host derives the clock the
-//     matrix cores ran at.
+//     matrix cores ran at.  The operands are either small constants built
+//     from the thread index or random codes loaded once from a buffer: the
+//     matrix cores draw more power when their inputs toggle, and the clock
+//     shows it.
+//   f8probe_mfma_lds: the GEMM's K loop without its global -> LDS copies: the
+//     same waves and MFMAs, each wave reading its A and B fragments for every
+//     64-byte K step from two 64 KB LDS stages (256 A rows and 256 B rows of
+//     128 bytes, 16-byte chunks XOR-swizzled by row pair, the GEMM's layout),
+//     filled once with random codes; the next step's fragments are read while
+//     the current step's MFMAs run, and the workgroup meets at a barrier once
+//     per 128-byte K block, as the GEMM does.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,16 +78,30 @@ __global__ __launch_bounds__(512) void stream_kernel(const u32x4 *__restrict__ s
 }
 
 // Eight accumulator tiles per wave, `iters` rounds of eight MFMAs.  The
-// operands are built from the thread index so the compiler cannot fold them;
+// operands are built from the thread index (ops == nullptr) or loaded from
+// ops (48 words per thread, thread-major), so the compiler cannot fold them;
 // the accumulators' sum is stored once, so the loop cannot be removed.  The
 // 128 accumulators and 48 operand registers (~178 VGPRs) allow two waves per
 // SIMD, so each CU holds one workgroup of eight waves, as the GEMM does.
-__global__ __launch_bounds__(512) void mfma_kernel(int iters, float *__restrict__ sink, uint64_t *__restrict__ clocks) {
+__global__ __launch_bounds__(512) void mfma_kernel(int iters, const int *__restrict__ ops, float *__restrict__ sink,
+                                                   uint64_t *__restrict__ clocks) {
   v8i a[4], b[2];
+  if (ops) {
+    const int *p = ops + (int64_t)(blockIdx.x * blockDim.x + threadIdx.x) * 48;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = v8i{(int)threadIdx.x + i, 1, 2, 3, 4, 5, 6, 7};
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) b[j] = v8i{(int)threadIdx.x ^ j, 7, 6, 5, 4, 3, 2, 1};
+      for (int e = 0; e < 8; ++e) a[i][e] = p[i * 8 + e];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[j][e] = p[32 + j * 8 + e];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = v8i{(int)threadIdx.x + i, 1, 2, 3, 4, 5, 6, 7};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = v8i{(int)threadIdx.x ^ j, 7, 6, 5, 4, 3, 2, 1};
+  }
   v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -94,6 +118,82 @@ __global__ __launch_bounds__(512) void mfma_kernel(int iters, float *__restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// 16-byte chunk c (0..7) of LDS row r (0..511) of one 64 KB stage.
+__device__ __forceinline__ int chunk_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// Fragment of row r for 64-byte K step ks (0/1) of a stage: lanes 0-31 take
+// the step's first 32 bytes, lanes 32-63 the second 32.
+__device__ __forceinline__ v8i lds_frag(const u32x4 *st, int r, int ks) {
+  const int c = ks * 4 + (threadIdx.x & 32 ? 2 : 0);
+  const u32x4 lo = st[chunk_slot(r, c)], hi = st[chunk_slot(r, c + 1)];
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// `iters` K blocks of 128 bytes over two LDS stages filled once from src
+// (8192 chunks of 16 bytes); per block and wave: 16 MFMAs, 24 fragment reads
+// of 16 bytes, one barrier.
+__global__ __launch_bounds__(512) void mfma_lds_kernel(const u32x4 *__restrict__ src, int iters,
+                                                       float *__restrict__ sink, uint64_t *__restrict__ clocks) {
+  __shared__ __attribute__((aligned(1024))) u32x4 st[2 * 4096];
+  for (int i = threadIdx.x; i < 2 * 4096; i += blockDim.x) st[i] = src[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave / 4) * 128, wn = 256 + (wave % 4) * 64;  // B rows follow the 256 A rows
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  v8i fa[4], fb[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = lds_frag(st, wm + i * 32 + (lane & 31), 0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[j] = lds_frag(st, wn + j * 32 + (lane & 31), 0);
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // the next step: this block's second half, or the next block's first
+      const u32x4 *nst = st + ((ks == 0 ? it : it + 1) & 1) * 4096;
+      const int nks = ks ^ 1;
+      v8i na[4], nb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) na[i] = lds_frag(nst, wm + i * 32 + (lane & 31), nks);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) nb[j] = lds_frag(nst, wn + j * 32 + (lane & 31), nks);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = nb[j];
+    }
+    __syncthreads();
   }
   float s = 0.0f;
 #pragma unroll
@@ -136,12 +236,22 @@ int f8probe_stream(int mode, const void *src, void *dst, int64_t n_bytes, int gr
   return (int)hipGetLastError();
 }
 
-// grid workgroups of 512 threads (eight waves); sink: grid * 512 floats;
-// clocks: 2 * grid uint64 {shader-clock cycles, 100 MHz ticks} per workgroup.
-// Flops: grid * 8 waves * iters * 8 * 131072.
-int f8probe_mfma(int grid, int iters, float *sink, uint64_t *clocks, void *stream) {
+// grid workgroups of 512 threads (eight waves); ops: NULL (operands from the
+// thread index) or grid * 512 * 48 int32 words of operand codes; sink:
+// grid * 512 floats; clocks: 2 * grid uint64 {shader-clock cycles, 100 MHz
+// ticks} per workgroup.  Flops: grid * 8 waves * iters * 8 * 131072.
+int f8probe_mfma(int grid, int iters, const void *ops, float *sink, uint64_t *clocks, void *stream) {
   if (grid < 1 || iters < 1 || !sink || !clocks) return (int)hipErrorInvalidValue;
-  mfma_kernel<<<grid, 512, 0, (hipStream_t)stream>>>(iters, sink, clocks);
+  mfma_kernel<<<grid, 512, 0, (hipStream_t)stream>>>(iters, (const int *)ops, sink, clocks);
+  return (int)hipGetLastError();
+}
+
+// As f8probe_mfma, fragments read from LDS: src holds 131072 bytes of
+// operand codes (two 64 KB stages) that every workgroup copies in once.
+// Flops: grid * 8 waves * iters * 16 * 131072.
+int f8probe_mfma_lds(int grid, int iters, const void *src, float *sink, uint64_t *clocks, void *stream) {
+  if (grid < 1 || iters < 1 || !src || !sink || !clocks) return (int)hipErrorInvalidValue;
+  mfma_lds_kernel<<<grid, 512, 0, (hipStream_t)stream>>>((const u32x4 *)src, iters, sink, clocks);
   return (int)hipGetLastError();
 }
 
