@@ -782,6 +782,14 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;
       launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+    } else if (use_big && tiles >= 8 * kCUs) {
+      // Eight or more rounds of tiles: groups of eight tile-rows, so that an
+      // XCD's 32 concurrent tiles form an 8 x 4 patch instead of 4 x 8
+      // (measured, same box: 65536 x 4096 x 4096 forward 907 -> 878 us, its
+      // backward pair 1682 -> 1669 us; with one to four rounds the two
+      // patches are level within noise, or 4 x 8 is ahead: 4096^3 57.7 vs
+      // 58.3 us).
+      launch_tiled<FA, FB, 256, 256, 2, 4, 1, 8, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_big) {
       launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_med) {

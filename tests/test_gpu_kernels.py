@@ -217,7 +217,10 @@ def _gemm_gpu(f8, a, fa, b, fb, inv_a, inv_b):
                                  # second half skipped) and 80 bytes (not skipped)
                                  (4096, 4096, 1600), (8192, 2048, 208),
                                  # exactly one 128x128 tile per CU: taken by the 64x128 tiles
-                                 (1024, 4096, 256)])
+                                 (1024, 4096, 256),
+                                 # more than eight rounds of 256x256 tiles (groups of eight tile-rows),
+                                 # 129 x 17 tiles with ragged last rows and columns
+                                 (33008, 4144, 512)])
 def test_gemm_matches_oracle(f8, fa, fb, mnk):
     M, N, K = mnk
     print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
