@@ -442,42 +442,60 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
 
     // Epilogue.  Lane (column c = lane & 31, half h = lane >> 5) holds, per
     // 32x32 tile, rows 8*(v>>2) + 4*h + (v&3) for v = 0..15.  Even lanes take
-    // column pair (c, c+1) at even v, odd lanes (c-1, c) at odd v, exchanging
-    // the missing value with the neighbour lane; the pair is one 32-bit LDS
-    // word.  Rows of even / odd v differ in parity and rows of the two halves
-    // in bit 2 (which swaps the 64-byte halves of the row), so each write is
-    // free of bank conflicts.
+    // column pair (c, c+1) at even v, odd lanes (c-1, c) at odd v: each lane
+    // keeps one of its values v = 2k, 2k+1 and sends the other to the
+    // neighbour lane (a DPP swap folded into the scaling multiply); the pair,
+    // rounded to bf16 as (kept, received), is one 32-bit LDS word, its halves
+    // swapped on odd lanes (a rotate by a per-lane amount).  Rows of even /
+    // odd v differ in parity and rows of the two halves in bit 2 (which swaps
+    // the 64-byte halves of the row), so each write is free of bank conflicts.
     __syncthreads();  // every wave is done with the stage buffers
     const float alpha = inv_a * inv_b;
     uint8_t *wreg = smem + wave * (WTM * RB);
     const bool odd = lane & 1;
-    // bias of this lane's column pair (cpair, cpair + 1) of each 32-column tile j
-    float bias_lo[TN], bias_hi[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int gc = n0 + wn + j * 32 + (lane & 30);
-      uint32_t bw = 0;
-      if (P.bias && gc < N) bw = *(const uint32_t *)(P.bias + gc);
-      bias_lo[j] = __uint_as_float(bw << 16);
-      bias_hi[j] = __uint_as_float(bw & 0xFFFF0000u);
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
+    const uint32_t rot = odd ? 16u : 0u;
+    auto stage_out = [&](auto BIAS) {
+      // bias of the kept and the received value of this lane's column pair
+      // (cpair, cpair + 1) of each 32-column tile j
+      float bias_keep[TN], bias_recv[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int cpair = j * 32 + (lane & 30);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float ve = acc[i][j][2 * k] * alpha, vo = acc[i][j][2 * k + 1] * alpha;
-          const float send = odd ? ve : vo;
-          const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
-          const f32x2 pair = odd ? f32x2{recv + bias_lo[j], vo + bias_hi[j]} : f32x2{ve + bias_lo[j], recv + bias_hi[j]};
-          const int v = 2 * k + (odd ? 1 : 0);
-          const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          *(bf16x2 *)(wreg + row * RB + ((cpair * 2) ^ (((row >> 2) & 1) << 6))) =
-              __builtin_convertvector(pair, bf16x2);
+        bias_keep[j] = bias_recv[j] = 0.0f;
+        if constexpr (decltype(BIAS)::value) {
+          const int gc = n0 + wn + j * 32 + (lane & 30);
+          const uint32_t bw = gc < N ? *(const uint32_t *)(P.bias + gc) : 0u;
+          const float lo = __uint_as_float(bw << 16), hi = __uint_as_float(bw & 0xFFFF0000u);
+          bias_keep[j] = odd ? hi : lo;
+          bias_recv[j] = odd ? lo : hi;
         }
       }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int cpair = j * 32 + (lane & 30);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
+            const float keep = odd ? a1 : a0, send = odd ? a0 : a1;
+            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+            float ks = keep * alpha, rs = recv * alpha;
+            if constexpr (decltype(BIAS)::value) {
+              ks += bias_keep[j];
+              rs += bias_recv[j];
+            }
+            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ks, rs}, bf16x2));
+            const int v = 2 * k + (odd ? 1 : 0);
+            const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            *(uint32_t *)(wreg + row * RB + ((cpair * 2) ^ (((row >> 2) & 1) << 6))) =
+                __builtin_amdgcn_alignbit(w, w, rot);
+          }
+        }
+    };
+    if (P.bias)
+      stage_out(bool_t<true>());
+    else
+      stage_out(bool_t<false>());
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     // All of the wave's staged chunks are read first, then stored with
