@@ -288,8 +288,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       kcb[j] = c * 16;
     }
     // copy q (0 .. LQ-1) of K block kt into stage kt & 1
+    // Tiles in odd bands of eight tile-columns walk K from the end (whole K
+    // blocks only, so no ragged block moves): an XCD's tiles advance a patch
+    // along a row band, and the patch that follows reads the same A rows
+    // starting with the K blocks its predecessor read last, still in the L2.
+    // The direction is a function of the tile alone, so a problem gives the
+    // same bits in any launch or batch (measured, same box: the Llama-8B
+    // layer's backward pairs 414.7 -> 402.5 us, its step 5195 -> 5088 us;
+    // the 65536-row step 3043 -> 3017 us).
+    const int nkb = (K + kBK - 1) / kBK;
+    const bool rev = ((tn >> 3) & 1) && K % kBK == 0;
     auto issue_one = [&](int kt, int q) {
-      const int k0 = kt * kBK;
+      const int k0 = (rev ? nkb - 1 - kt : kt) * kBK;
       uint8_t *stage = smem + (kt & 1) * STB;
       if (q < LA) {
         const int vo = (kca[q] + k0 < K) ? offa[q] + k0 : kOutOfRange;  // past K: outside the range -> 0
