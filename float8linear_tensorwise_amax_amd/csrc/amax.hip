@@ -39,6 +39,11 @@ static_assert(kMaxGrid * kMaxAmaxTensors + kWsPartialsOffset <= (int)(kWorkspace
               "partials do not fit the workspace");
 
 // Max magnitude (15-bit) over this thread's grid-stride share of x[0, n).
+// The grid sweeps the tensor from its end to its start: the cast that
+// follows walks it from the start, so the last lines this pass leaves in the
+// last-level cache are the first ones the cast reads (measured, same box: the
+// 65536-row linear's amax + cast of X and W 311 -> 306 us, of dY 292 -> 287
+// us, its step 3067 -> 3050 us).
 __device__ __forceinline__ uint32_t thread_magmax(const uint16_t *__restrict__ x, int64_t n, int64_t gtid,
                                                   int64_t nthreads) {
   const u32x4 *__restrict__ xv = reinterpret_cast<const u32x4 *>(x);
@@ -48,7 +53,7 @@ __device__ __forceinline__ uint32_t thread_magmax(const uint16_t *__restrict__ x
   for (; i + (kUnroll - 1) * nthreads < nv; i += kUnroll * nthreads) {
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = xv[i + u * nthreads];
+    for (int u = 0; u < kUnroll; ++u) v[u] = xv[nv - 1 - (i + u * nthreads)];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       m = mag_max2(m, v[u].x);
@@ -58,7 +63,7 @@ __device__ __forceinline__ uint32_t thread_magmax(const uint16_t *__restrict__ x
     }
   }
   for (; i < nv; i += nthreads) {
-    const u32x4 v = xv[i];
+    const u32x4 v = xv[nv - 1 - i];
     m = mag_max2(m, v.x);
     m = mag_max2(m, v.y);
     m = mag_max2(m, v.z);
