@@ -52,7 +52,8 @@
  *    caller's next synchronisation.  Data-dependent conditions (NaN, Inf)
  *    are not errors.
  *  - Calls that share a workspace or a scaling state must be ordered (same
- *    stream, or synchronised); the library keeps no global mutable state.
+ *    stream, or synchronised).  The library keeps no global mutable state,
+ *    except the per-device static scratch of f8lin_backward_noalloc.
  */
 #ifndef F8LIN_H_
 #define F8LIN_H_
@@ -80,12 +81,15 @@ typedef enum { F8LIN_E4M3 = 0, F8LIN_E5M2 = 1 } f8lin_fmt;
  *         max into one of eight group slots; the last workgroup of a group
  *         folds the group into the tensor's slot, and the last group
  *         publishes the amax (one launch, no fences).
- * TWOPASS: every workgroup writes its partial max; a second one-workgroup
- *          launch reduces the partials. */
+ * TWOPASS: every workgroup writes its partial max; a second pass reduces
+ *          the partials: a one-workgroup launch in f8lin_amax, the cast
+ *          kernel's prologue in f8lin_forward / f8lin_backward. */
 typedef enum { F8LIN_AMAX_ATOMIC = 0, F8LIN_AMAX_TWOPASS = 1 } f8lin_amax_algo;
 
-/* DYNAMIC: the scale comes from state->amax, written beforehand by
- *          f8lin_amax for the same tensor.
+/* DYNAMIC: the scale comes from the tensor's current amax in state->amax:
+ *          for f8lin_cast_transpose written beforehand by f8lin_amax; for
+ *          f8lin_forward / f8lin_backward computed by the call itself (or
+ *          handed in, with x_amax_given / dy_amax_given).
  * DELAYED: the scale comes from max(state->history[0..15]) (past steps only),
  *          and the cast also folds this tensor's amax into state->amax
  *          (which must hold 0 or a smaller value: f8lin_delayed_update resets
