@@ -14,10 +14,10 @@
 //     cbsz / blgp.  A lane feeds the same 32 K-bytes of its A row and of its
 //     B row, so A and B share one K order and the instruction's internal K
 //     order cannot matter.
-//   * Two waves per SIMD (an issue-rate probe: one wave per SIMD reached
-//     ~75-85% of the MFMA rate, two waves ~97%).  Workgroups:
-//       big   256 x 256 tile, 8 waves (2 x 4), wave tile 128 x 64
-//             (128 fp32 accumulators per lane), one workgroup per CU;
+//   * Workgroups:
+//       big   256 x 256 tile, 4 waves (2 x 2, one per SIMD), wave tile
+//             128 x 128 (256 fp32 accumulators per lane, in the AGPRs), one
+//             workgroup per CU, with its own K loop (below);
 //       small 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64, two per CU,
 //             for problems with too few big tiles to fill 256 CUs, or
 //             whose ragged edge would leave the last round of big tiles
@@ -34,14 +34,25 @@
 //   * LDS slot of (row r, 16-byte chunk c) = r*8 + (c ^ ((r>>1) & 7)): every
 //     16 consecutive rows at one chunk fall in 16 distinct bank groups, so
 //     the 128-bit fragment reads are conflict-free.
-//   * Schedule (fixed with scheduling fences, since the compiler otherwise
-//     clusters the LDS reads after the MFMAs and the waves stall on them):
-//     MFMAs go column by column over the wave tile; each fragment register is
-//     refilled from LDS right after its last MFMA, at least three MFMAs before
-//     its next use.  One barrier per K block sits after the first column of
-//     its second half: it publishes block k+1 (each wave first waits for its
-//     own copies) and retires block k, whose buffer then receives block k+2;
-//     those copies are spread between the MFMAs that follow.
+//   * Schedule of the small and medium tiles (two waves per SIMD; fixed with
+//     scheduling fences, since the compiler otherwise clusters the LDS reads
+//     after the MFMAs and the waves stall on them): MFMAs go column by
+//     column over the wave tile; each fragment register is refilled from LDS
+//     right after its last MFMA, at least three MFMAs before its next use.
+//     One barrier per K block sits after the first column of its second
+//     half: it publishes block k+1 (each wave first waits for its own copies)
+//     and retires block k, whose buffer then receives block k+2; those copies
+//     are spread between the MFMAs that follow.
+//   * The big tile's K loop (one wave per SIMD, so nothing hides a wave's
+//     stall but its own schedule): each block's A fragments (both K halves)
+//     are read from LDS in one 16-MFMA step and its B fragments in the next,
+//     so the A and B regions of a stage are freed one step apart and each
+//     step refills one region: every step issues the same eighth of a
+//     block's copies, and a copy has two to three steps to land before it is
+//     read (the fragments of three half-blocks, 192 VGPRs, are held).  On
+//     4096 x 4096 x 16384 this keeps the matrix cores ~89-95% busy against
+//     ~83% for two waves per SIMD with a 128 x 64 wave tile, which read
+//     1.5x the LDS bytes per flop.
 //   * The matrix cores and the memory system together exceed the chip's power
 //     budget: the shader clock drops from 2.4 GHz to ~1.7-2.0 GHz while this
 //     loop runs (read with s_memtime against the constant-rate counter), so
@@ -78,6 +89,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
+constexpr int kMinBigK = 4 * kBK;  // shortest K the 256 x 256 tiles take
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 // Every matrix dimension is at most 2^22 (checked at the C ABI), so a tile's
@@ -117,6 +129,19 @@ __device__ __forceinline__ void tile_coords(int local, int tiles_m, int tiles_n,
 
 template <bool B>
 using bool_t = std::integral_constant<bool, B>;
+template <int V>
+using int_t = std::integral_constant<int, V>;
+// The lane index (0-63), produced by an instruction the compiler cannot move:
+// kernels at the register limit call this where they need it instead of
+// keeping it live (a spilled value's reload waits for all memory operations
+// in flight, copies and stores included).
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+// block parity of the step k steps after one of parity (p0, h0)
+constexpr int step_p(int p0, int h0, int k) { return (p0 + ((h0 + k) >> 1)) & 1; }
 
 // PARTIAL: every problem is split along K into P.splits ranges of whole K
 // blocks; the tile list holds every (range, tile) pair, and a tile writes its
@@ -144,10 +169,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   constexpr int LA = OPA / 1024 / NW, LB = OPB / 1024 / NW;  // 1 KB copies per wave per stage
   constexpr int LQ = LA + LB;
   constexpr int RB = WTN * 2;  // bytes per staged output row
+  // 256 x 256 tiles with four waves take the K loop below that holds three
+  // half-blocks of fragments in registers; the others two waves per SIMD
+  constexpr bool kStag = BM == 256 && BN == 256 && NW == 4;
   static_assert(LA >= 1 && LB >= 1 && TM >= 1 && TN >= 2, "tile configuration");
   static_assert(!(DYN && PARTIAL), "split problems keep the fixed stride");
   static_assert(!(AMAX && PARTIAL), "split problems take their amax in the reduce kernel");
-  static_assert(LQ <= 15, "vmcnt immediate");
+  static_assert(kStag || LQ <= 15, "vmcnt immediate");
   static_assert(NW * WTM * RB <= 2 * STB, "epilogue staging must fit in LDS");
   // two stages of A and B (the epilogue reuses them for its staging); DYN
   // also keeps its two next-item slots past them and AMAX one word per wave,
@@ -156,7 +184,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   constexpr int kDynBytes = DYN ? 16 : 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STB + kDynBytes + (AMAX ? 4 * 64 * NW : 0)];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // (with 256 x 256 tiles the wave index is held as a scalar: a vector copy
+  // would be spilled and reloaded at every tile)
+  const int wave = kStag ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int g = lane >> 5;  // K half within a 64-byte sub-step
   const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
 
@@ -167,14 +198,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
   const int xcd = (int)blockIdx.x % kXcds, local_wg = (int)blockIdx.x / kXcds;
   const int nwg = (int)gridDim.x;
   const int wx = nwg / kXcds + (xcd < nwg % kXcds ? 1 : 0);
-  int start[kMaxGemms], len[kMaxGemms], total = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxGemms; ++i) {
+  // start / length of this XCD's share of problem i (scalar arithmetic,
+  // redone per tile rather than kept in registers across the K loop)
+  auto share = [&](int i, int &start_i, int &len_i) {
     const int T = i < batch.count ? batch.p[i].tiles_m * batch.p[i].tiles_n * (PARTIAL ? batch.p[i].splits : 1) : 0;
     const int per = T / kXcds, rem = T % kXcds;
-    start[i] = xcd * per + min(xcd, rem);
-    len[i] = per + (xcd < rem ? 1 : 0);
-    total += len[i];
+    start_i = xcd * per + min(xcd, rem);
+    len_i = per + (xcd < rem ? 1 : 0);
+  };
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxGemms; ++i) {
+    int st, ln;
+    share(i, st, ln);
+    total += ln;
   }
 
   // DYN: item wx + i goes to the workgroup whose fetch returned i.  Thread 0
@@ -227,14 +264,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       }
     };
     // problem pi, tile t of it: this XCD's shares of the problems follow one another
-    int pi = 0, off = it;
+    int pi = 0, off = it, t = 0;
 #pragma unroll
-    for (int i = 0; i + 1 < kMaxGemms; ++i)
-      if (pi == i && off >= len[i]) {
-        off -= len[i];
-        pi = i + 1;
+    for (int i = 0; i < kMaxGemms; ++i) {
+      int st, ln;
+      share(i, st, ln);
+      if (pi == i) {
+        if (off >= ln && i + 1 < kMaxGemms) {
+          off -= ln;
+          pi = i + 1;
+        } else {
+          t = st + off;
+        }
       }
-    int t = start[pi] + off;
+    }
     if constexpr (AMAX) {
       if (pi != amax_pi) {  // uniform: the workgroup moves on to another problem
         if (amax_pi >= 0) flush_amax();
@@ -333,95 +376,301 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    v8i fa[TM], fb[TN];
     auto mfma = [&](const v8i &a, const v8i &b, v16f &c) {
       c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
     };
-    auto col0 = [&]() {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) mfma(fa[i], fb[0], acc[i][0]);
-    };
-    // Columns 1 .. TN-1 of the current sub-step.  With REFILL, fb[j] is
-    // refilled with sub-step (stage, ks) after column j and fa[i] after its
-    // MFMA in the last column (fb[0] was refilled by the caller); with
-    // kt >= 0, the LQ copies of K block kt are spread over these MFMAs.
-    auto cols = [&](auto REFILL, int stage, int ks, int kt) {
-      constexpr int nmf = (TN - 1) * TM;
-      int q = 0, mf = 0;
-#pragma unroll
-      for (int j = 1; j < TN; ++j) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          mfma(fa[i], fb[j], acc[i][j]);
-          if constexpr (decltype(REFILL)::value) {
-            if (j == TN - 1) fa[i] = rd(stage, 0, arow[i], ks);
-          }
-          ++mf;
-          if (kt >= 0) {
-            const int upto = (mf * LQ + nmf - 1) / nmf;
-            while (q < upto) issue_one(kt, q++);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (decltype(REFILL)::value) fb[j] = rd(stage, OPA, brow[j], ks);
-      }
-    };
-    // K block s: the fragments hold its sub-step 0 and column 0 is done.
-    // NEXT: a block s+1 exists; DMA: block s+2 exists (copied during this one).
     const int nk = (K + kBK - 1) / kBK;
     // A last K block with at most 64 bytes left (K = 1600, 4800) holds only
     // zeros in its second sub-step: those MFMAs would add exact zeros to
     // accumulators that can never be -0, so they are skipped (same bits).
     const bool tail_half = K - (nk - 1) * kBK <= kBK / 2;
-    auto block = [&](int s, auto NEXT, auto DMA) {
-      const int cb = s & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      fb[0] = rd(cb, OPA, brow[0], 1);
-      cols(bool_t<true>(), cb, 1, -1);  // rest of sub-step 0; fragments <- sub-step 1
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (decltype(NEXT)::value) {
-        col0();
+    if constexpr (!kStag) {
+      v8i fa[TM], fb[TN];
+      auto col0 = [&]() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) mfma(fa[i], fb[0], acc[i][0]);
+      };
+      // Columns 1 .. TN-1 of the current sub-step.  With REFILL, fb[j] is
+      // refilled with sub-step (stage, ks) after column j and fa[i] after its
+      // MFMA in the last column (fb[0] was refilled by the caller); with
+      // kt >= 0, the LQ copies of K block kt are spread over these MFMAs.
+      auto cols = [&](auto REFILL, int stage, int ks, int kt) {
+        constexpr int nmf = (TN - 1) * TM;
+        int q = 0, mf = 0;
+#pragma unroll
+        for (int j = 1; j < TN; ++j) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            mfma(fa[i], fb[j], acc[i][j]);
+            if constexpr (decltype(REFILL)::value) {
+              if (j == TN - 1) fa[i] = rd(stage, 0, arow[i], ks);
+            }
+            ++mf;
+            if (kt >= 0) {
+              const int upto = (mf * LQ + nmf - 1) / nmf;
+              while (q < upto) issue_one(kt, q++);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (decltype(REFILL)::value) fb[j] = rd(stage, OPA, brow[j], ks);
+        }
+      };
+      // K block s: the fragments hold its sub-step 0 and column 0 is done.
+      // NEXT: a block s+1 exists; DMA: block s+2 exists (copied during this one).
+      auto block = [&](int s, auto NEXT, auto DMA) {
+        const int cb = s & 1;
         __builtin_amdgcn_sched_barrier(0);
-        // block s+1 resident (own copies, then everyone's), every read of
-        // block s done everywhere: its buffer can take block s+2
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
+        fb[0] = rd(cb, OPA, brow[0], 1);
+        cols(bool_t<true>(), cb, 1, -1);  // rest of sub-step 0; fragments <- sub-step 1
         __builtin_amdgcn_sched_barrier(0);
-        fb[0] = rd(cb ^ 1, OPA, brow[0], 0);
-        cols(bool_t<true>(), cb ^ 1, 0, decltype(DMA)::value ? s + 2 : -1);
-        __builtin_amdgcn_sched_barrier(0);
-        col0();
-      } else if (!tail_half) {
-        col0();
-        __builtin_amdgcn_sched_barrier(0);
-        cols(bool_t<false>(), 0, 0, -1);
-      }
-    };
+        if constexpr (decltype(NEXT)::value) {
+          col0();
+          __builtin_amdgcn_sched_barrier(0);
+          // block s+1 resident (own copies, then everyone's), every read of
+          // block s done everywhere: its buffer can take block s+2
+          __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          fb[0] = rd(cb ^ 1, OPA, brow[0], 0);
+          cols(bool_t<true>(), cb ^ 1, 0, decltype(DMA)::value ? s + 2 : -1);
+          __builtin_amdgcn_sched_barrier(0);
+          col0();
+        } else if (!tail_half) {
+          col0();
+          __builtin_amdgcn_sched_barrier(0);
+          cols(bool_t<false>(), 0, 0, -1);
+        }
+      };
 
-    if (nk > 0) {
+      if (nk > 0) {
 #pragma unroll
-      for (int q = 0; q < LQ; ++q) issue_one(0, q);
-      if (nk > 1) {
+        for (int q = 0; q < LQ; ++q) issue_one(0, q);
+        if (nk > 1) {
 #pragma unroll
-        for (int q = 0; q < LQ; ++q) issue_one(1, q);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | LQ);  // vmcnt(LQ): block 0 resident
+          for (int q = 0; q < LQ; ++q) issue_one(1, q);
+          __builtin_amdgcn_s_waitcnt(0x0F70 | LQ);  // vmcnt(LQ): block 0 resident
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        __builtin_amdgcn_s_barrier();
+        publish();
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = rd(0, OPA, brow[j], 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = rd(0, 0, arow[i], 0);
+        col0();
+        int s = 0;
+        for (; s + 2 < nk; ++s) block(s, bool_t<true>(), bool_t<true>());
+        if (s + 1 < nk) block(s++, bool_t<true>(), bool_t<false>());
+        block(s, bool_t<false>(), bool_t<false>());
       } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the fetch has returned
+        publish();
       }
+    } else {
+      // Four waves of 128 x 128 (one per SIMD).  A region is one operand of
+      // one K block: region 2 kb + X (X = 0: A, 1: B); consecutive blocks
+      // alternate between the two stages.
+      // Step j = 2 s + h runs the 16 MFMAs of K block s, half h, from
+      // registers; meanwhile it reads all fragments of region j + 2 (both
+      // halves of one operand of block s + 1) and copies region j + 5 over
+      // region j + 1, which step j - 1 finished reading.  So every step
+      // issues the same share of copies, and a copy has two to three steps to
+      // land before its region is read; the fragments of three half-blocks
+      // are held in registers.  The barrier of step j sits after its second
+      // MFMA: each wave has then finished the reads of step j - 1 and
+      // received all its copies of region j + 2.
+      static_assert(TM == 4 && TN == 4 && LA == 8 && LB == 8 && OPA == OPB, "four 128 x 128 wave tiles");
+      // An odd count of K blocks gets a virtual block at the end (its copies
+      // re-read a real block, its two steps -- MFMAs only -- are skipped), so
+      // that the pipeline always runs an even count nkp and one sequence of
+      // steps.
+      const int virt = nkb & 1, nkp = nkb + virt;
+      const int swave = wave;  // (a scalar here)
+      // lane-derived addresses are computed per tile from a regenerated lane
+      // index (kept across the tile loop they would be spilled, and a spill
+      // reload waits for every copy and store in flight)
+      const int kl = lane_here();
+      // Layout: A of stages 0 and 1, then B of stages 0 and 1, so that every
+      // fragment read of one operand is a lane base plus an immediate offset
+      // below 64 KB (four bases per operand).
+      auto region = [&](int S, int X) { return smem + X * 2 * OPA + S * OPA; };
+      // Byte offset, within a region, of this lane's 16-byte chunk lo (0/1)
+      // of K half hh in fragment 0 of operand X: row r = w + l (w the wave's
+      // first row, a multiple of 16; l = lane & 31), chunk c = 4 hh + 2 (lane
+      // >> 5) + lo, at slot128(r, c); fragment f is 32 rows (4096 bytes) on.
+      int rdb[2][2][2];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int lo = 0; lo < 2; ++lo) {
+            const int l = kl & 31, c = hh * 4 + (kl >> 5) * 2 + lo;
+            rdb[X][hh][lo] = ((X ? wn : wm) + l) * 128 + ((c ^ ((l >> 1) & 7)) << 4);
+          }
+      auto rd2 = [&](int S, int X, int f, int hh) {
+        const uint8_t *st = region(S, X) + f * 4096;
+        const u32x4 lo = *(const u32x4 *)(st + rdb[X][hh][0]), hi = *(const u32x4 *)(st + rdb[X][hh][1]);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      v8i fa2[2][2][TM], fb2[2][2][TN];  // [block parity][K half][fragment]
+      // Copy q's slots (LA = 8) start 16 (q >> 1) rows past those of copy
+      // q & 1: its global offset is one of two per-lane bases plus a uniform
+      // row step, and its K byte the base's chunk.
+      int cbase_a[2], cbase_b[2], kc[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = swave * 64 + (kl >> 3) + 8 * e;
+        kc[e] = 16 * ((kl & 7) ^ (kl >> 4) ^ (e << 2));
+        cbase_a[e] = r * lda + kc[e];
+        cbase_b[e] = r * ldb + kc[e];
+      }
+      // K block order: with a ragged K the ragged (physical last) block goes
+      // first, so that only the prologue's copies need a per-lane K mask;
+      // otherwise forward, or from the end on odd tile bands (above).
+      const bool ragged = K % kBK != 0;
+      // Copy q of region (X, pipeline block kb) into stage S.  The row stays
+      // in the per-lane offset (rows past the tile fail the range check) and
+      // the block's K offset rides in the scalar offset.  MODE 0: a whole
+      // block (or the virtual one); 1: a block of the prologue, which may be
+      // the ragged one (lanes whose 16 bytes start at or past K out of range,
+      // which loads zeros: K is a multiple of 16).
+      // The K byte offset of pipeline block kb >= 1 is linear in kb (kept in
+      // scalar registers): forward from -ragged blocks, or backward from nkb - 1
+      // (odd tile bands); clamped to the whole blocks for the virtual one.
+      const int kstep = __builtin_amdgcn_readfirstlane(rev ? -kBK : kBK);
+      const int k00 = __builtin_amdgcn_readfirstlane(rev ? (nkb - 1) * kBK : (ragged ? -kBK : 0));
+      const int kmax = __builtin_amdgcn_readfirstlane((nkb - 1 - (ragged ? 1 : 0)) * kBK);
+      // row steps of the copies (16 rows per pair of copies), scalar
+      const int rstep_a = __builtin_amdgcn_readfirstlane(16 * lda), rstep_b = __builtin_amdgcn_readfirstlane(16 * ldb);
+      auto copy_region = [&](auto X_, auto S_, auto MODE_, int kb, int q) {
+        constexpr int X = decltype(X_)::value, S = decltype(S_)::value, MODE = decltype(MODE_)::value;
+        lds_void *dst = (lds_void *)(region(S, X) + (swave * LA + q) * 1024);
+        // Row offset: the lane's base plus a multiple of the scalar row step,
+        // added by an opaque instruction so that the compiler does not hold
+        // all sixteen offsets in registers across the K loop.
+        int vrow = X == 0 ? cbase_a[q & 1] : cbase_b[q & 1];
+        if ((q >> 1) > 0) {  // (q is known after unrolling)
+          const int st = (q >> 1) * (X == 0 ? rstep_a : rstep_b);
+          asm volatile("v_add_u32 %0, %1, %2" : "=v"(vrow) : "s"(st), "v"(vrow));
+        }
+        if constexpr (MODE == 0) {
+          const int k0 = min(max(k00 + kb * kstep, 0), kmax);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? rsa : rsb, dst, 16, vrow, k0, 0, 0);
+        } else {
+          const int kp = rev ? nkb - 1 - kb : (ragged ? (kb == 0 ? nkb - 1 : kb - 1) : kb);
+          const int k0 = kp * kBK;
+          const int vo = kc[q & 1] + k0 < K ? vrow : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? rsa : rsb, dst, 16, vo, __builtin_amdgcn_readfirstlane(k0),
+                                                   0, 0);
+        }
+      };
+      auto copy_all = [&](auto X_, auto S_, int kb) {
+#pragma unroll
+        for (int q = 0; q < LA; ++q) copy_region(X_, S_, int_t<1>(), kb, q);
+      };
+      // MFMA slots of a step's fragment reads (half 0 fragments 0-3, then
+      // half 1) and copies, after the barrier
+      constexpr int kRdSlot[16] = {-1, -1, 0, 1, 2, -1, 3, 4, -1, 5, 6, -1, 7, -1, -1, -1};
+      constexpr int kCpSlot[16] = {-1, -1, 0, -1, 1, -1, 2, -1, 3, -1, 4, -1, 5, 6, -1, 7};
+      // step j (block parity P, half H); RD / CP: whether region j + 2 / j + 5
+      // exist; MODE: the copies' kind; VM: copies of this wave that may still
+      // be in flight at the barrier (those of regions j + 3 and j + 4 that
+      // exist); BAR: whether the step needs the barrier at all (the last two
+      // do not)
+      auto step = [&](auto P_, auto H_, auto RD, auto CP, auto MODE, auto BAR, int vm, int j) {
+        constexpr int P = decltype(P_)::value, H = decltype(H_)::value;
+        constexpr int RP = P ^ 1, CS = H == 0 ? P : P ^ 1;
+        const int ckb = (j + 5) >> 1;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          mfma(fa2[P][H][t & 3], fb2[P][H][t >> 2], acc[t & 3][t >> 2]);
+          if (t == 1 && BAR) {
+            if (vm >= 16)
+              __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) lgkmcnt(0)
+            else if (vm >= 8)
+              __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0)
+            else
+              __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+          }
+          if (RD && kRdSlot[t] >= 0) {
+            const int f = kRdSlot[t] & 3, hh = kRdSlot[t] >> 2;
+            if constexpr (H == 0)
+              fa2[RP][hh][f] = rd2(RP, 0, f, hh);
+            else
+              fb2[RP][hh][f] = rd2(RP, 1, f, hh);
+          }
+          if (CP && kCpSlot[t] >= 0) copy_region(int_t<H ^ 1>(), int_t<CS>(), MODE, ckb, kCpSlot[t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      const auto T = bool_t<true>();
+      auto full = [&](auto P_, auto H_, int j) { step(P_, H_, T, T, int_t<0>(), T, 16, j); };
+      // A step d steps before the last one (d <= 6): it reads region j + 2
+      // while d >= 2, copies region j + 5 (the last block's) while d >= 5,
+      // and may leave in flight the copies of the regions after j + 2 that
+      // exist (two while d >= 4, one at d = 3).
+      auto tstep = [&](auto D_, auto P_, auto H_, int j) {
+        constexpr int d = decltype(D_)::value;
+        if constexpr (d >= 2) {
+          step(P_, H_, T, bool_t<(d >= 5)>(), int_t<0>(), T, d >= 4 ? 16 : (d == 3 ? 8 : 0), j);
+        } else {
+          // the last block: MFMAs only; skipped whole when it is the virtual one
+          if (!virt) step(P_, H_, bool_t<false>(), bool_t<false>(), int_t<0>(), bool_t<false>(), 0, j);
+        }
+      };
+      // steps j .. j + D0 (d = D0 .. 0), the first of parity (P0, H0)
+      auto tail = [&](auto D0_, auto P0_, auto H0_, int j) {
+        constexpr int D0 = decltype(D0_)::value, p0 = decltype(P0_)::value, h0 = decltype(H0_)::value;
+        static_assert(D0 <= 6, "tail length");
+        tstep(int_t<D0>(), int_t<p0>(), int_t<h0>(), j);
+        if constexpr (D0 >= 1) tstep(int_t<D0 - 1>(), int_t<step_p(p0, h0, 1)>(), int_t<(h0 + 1) & 1>(), j + 1);
+        if constexpr (D0 >= 2) tstep(int_t<D0 - 2>(), int_t<step_p(p0, h0, 2)>(), int_t<(h0 + 2) & 1>(), j + 2);
+        if constexpr (D0 >= 3) tstep(int_t<D0 - 3>(), int_t<step_p(p0, h0, 3)>(), int_t<(h0 + 3) & 1>(), j + 3);
+        if constexpr (D0 >= 4) tstep(int_t<D0 - 4>(), int_t<step_p(p0, h0, 4)>(), int_t<(h0 + 4) & 1>(), j + 4);
+        if constexpr (D0 >= 5) tstep(int_t<D0 - 5>(), int_t<step_p(p0, h0, 5)>(), int_t<(h0 + 5) & 1>(), j + 5);
+        if constexpr (D0 >= 6) tstep(int_t<D0 - 6>(), int_t<step_p(p0, h0, 6)>(), int_t<(h0 + 6) & 1>(), j + 6);
+      };
+
+      // (the host sends only problems of at least four K blocks here)
+      // Prologue: blocks 0 and 1 copied, block 0 read whole, then region 4
+      // (block 2's A) copied over block 0's A.  Block i sits in stage i & 1.
+      copy_all(int_t<0>(), int_t<0>(), 0);
+      copy_all(int_t<1>(), int_t<0>(), 0);
+      copy_all(int_t<0>(), int_t<1>(), 1);
+      copy_all(int_t<1>(), int_t<1>(), 1);
+      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): block 0 resident
       __builtin_amdgcn_s_barrier();
       publish();
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = rd(0, OPA, brow[j], 0);
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = rd(0, 0, arow[i], 0);
-      col0();
-      int s = 0;
-      for (; s + 2 < nk; ++s) block(s, bool_t<true>(), bool_t<true>());
-      if (s + 1 < nk) block(s++, bool_t<true>(), bool_t<false>());
-      block(s, bool_t<false>(), bool_t<false>());
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the fetch has returned
-      publish();
+        for (int f = 0; f < 4; ++f) {
+          fa2[0][hh][f] = rd2(0, 0, f, hh);
+          fb2[0][hh][f] = rd2(0, 1, f, hh);
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): block 0 read by this wave
+      __builtin_amdgcn_s_barrier();         // ... and by all
+      copy_all(int_t<0>(), int_t<0>(), 2);
+      full(int_t<0>(), int_t<0>(), 0);
+      int j = 1;
+      if (nkp > 4) {
+        // (the loop's first round peeled: the register allocator then keeps
+        // the fragments where the loop wants them)
+        full(int_t<0>(), int_t<1>(), 1);
+        full(int_t<1>(), int_t<0>(), 2);
+        full(int_t<1>(), int_t<1>(), 3);
+        full(int_t<0>(), int_t<0>(), 4);
+        for (j = 5; j + 4 <= 2 * nkp - 7; j += 4) {
+          full(int_t<0>(), int_t<1>(), j);
+          full(int_t<1>(), int_t<0>(), j + 1);
+          full(int_t<1>(), int_t<1>(), j + 2);
+          full(int_t<0>(), int_t<0>(), j + 3);
+        }
+      }
+      tail(int_t<6>(), int_t<0>(), int_t<1>(), j);
     }
 
     if constexpr (PARTIAL) {
@@ -433,14 +682,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(reinterpret_cast<float *>(P.c) + ((int64_t)range * M + m0) * N), (short)0, rows_c * N * 4,
           0x00020000);
+      // (with 256 x 256 tiles the lane index is regenerated here: the
+      // addresses are derived per tile, not kept across the K loop)
+      const int pl = kStag ? lane_here() : lane;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn + j * 32 + (lane & 31);
+          const int col = n0 + wn + j * 32 + (pl & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (pl >> 5) + (v & 3);
             const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rsp, vo, 0, 0);
           }
@@ -457,12 +709,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     // neighbour lane (a DPP swap folded into the scaling multiply); the pair,
     // rounded to bf16 as (kept, received), is one 32-bit LDS word, its halves
     // swapped on odd lanes (a rotate by a per-lane amount).  Rows of even /
-    // odd v differ in parity and rows of the two halves in bit 2 (which swaps
-    // the 64-byte halves of the row), so each write is free of bank conflicts.
+    // odd v differ in parity and rows of the two halves in bit 2 (stage_swz
+    // moves them to other banks), so each write is free of bank conflicts.
     __syncthreads();  // every wave is done with the stage buffers
     const float alpha = inv_a * inv_b;
+    // The lane index of the epilogue: with 256 x 256 tiles regenerated here,
+    // so that the compiler derives the epilogue's addresses from it per tile
+    // instead of keeping them (spilled) across the K loop.
+    const int el = kStag ? lane_here() : lane;
+    // byte swizzle of a staged row: rows with bit 2 set swap their 64-byte
+    // halves; 256-byte rows (one full set of banks) also swap the 128-byte
+    // halves of odd rows, which the other lane of a column pair writes
+    auto stage_swz = [](int row) { return (((row >> 2) & 1) << 6) ^ (RB >= 256 ? (row & 1) << 7 : 0); };
     uint8_t *wreg = smem + wave * (WTM * RB);
-    const bool odd = lane & 1;
+    const bool odd = el & 1;
     const uint32_t rot = odd ? 16u : 0u;
     auto stage_out = [&](auto BIAS) {
       // bias of the kept and the received value of this lane's column pair
@@ -472,7 +732,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (int j = 0; j < TN; ++j) {
         bias_keep[j] = bias_recv[j] = 0.0f;
         if constexpr (decltype(BIAS)::value) {
-          const int gc = n0 + wn + j * 32 + (lane & 30);
+          const int gc = n0 + wn + j * 32 + (el & 30);
           const uint32_t bw = gc < N ? *(const uint32_t *)(P.bias + gc) : 0u;
           const float lo = __uint_as_float(bw << 16), hi = __uint_as_float(bw & 0xFFFF0000u);
           bias_keep[j] = odd ? hi : lo;
@@ -483,7 +743,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int cpair = j * 32 + (lane & 30);
+          const int cpair = j * 32 + (el & 30);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
@@ -496,9 +756,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
             }
             const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ks, rs}, bf16x2));
             const int v = 2 * k + (odd ? 1 : 0);
-            const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            *(uint32_t *)(wreg + row * RB + ((cpair * 2) ^ (((row >> 2) & 1) << 6))) =
-                __builtin_amdgcn_alignbit(w, w, rot);
+            const int row = i * 32 + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
+            *(uint32_t *)(wreg + row * RB + ((cpair * 2) ^ stage_swz(row))) = __builtin_amdgcn_alignbit(w, w, rot);
           }
         }
     };
@@ -516,28 +775,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     const int rows_c = min(BM, M - m0);
     const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(P.c + (int64_t)m0 * N), (short)0, (int)((uint32_t)rows_c * (uint32_t)N * 2u), 0x00020000);
-    u32x4 vals[NCH];
-    int offs[NCH];
+    // (in passes of at most 16 chunks per lane, to bound the registers held)
+    constexpr int PASS = NCH < 16 ? NCH : 16;
+    static_assert(NCH % PASS == 0, "epilogue passes");
     uint32_t omag = 0;  // AMAX: this lane's max magnitude of the values it stores
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int idx = k * 64 + lane;
-      const int row = idx / CPR, ch = idx % CPR;
-      vals[k] = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ (((row >> 2) & 1) << 6)));
-      const int gcol = n0 + wn + ch * 8;
-      offs[k] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
-      if constexpr (AMAX) {
-        // the values this chunk stores (padding rows may hold the bias: they do not count)
-        if (gcol < N && wm + row < rows_c)
-          omag = mag_max2(mag_max2(mag_max2(mag_max2(omag, vals[k].x), vals[k].y), vals[k].z), vals[k].w);
+    for (int k0 = 0; k0 < NCH; k0 += PASS) {
+      u32x4 vals[PASS];
+      int offs[PASS];
+#pragma unroll
+      for (int u = 0; u < PASS; ++u) {
+        const int idx = (k0 + u) * 64 + el;
+        const int row = idx / CPR, ch = idx % CPR;
+        vals[u] = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ stage_swz(row)));
+        const int gcol = n0 + wn + ch * 8;
+        offs[u] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
+        if constexpr (AMAX) {
+          // the values this chunk stores (padding rows may hold the bias: they do not count)
+          if (gcol < N && wm + row < rows_c)
+            omag = mag_max2(mag_max2(mag_max2(mag_max2(omag, vals[u].x), vals[u].y), vals[u].z), vals[u].w);
+        }
       }
-    }
-    if (batch.nt_stores) {
+      if (batch.nt_stores) {
 #pragma unroll
-      for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 2);  // nt
-    } else {
+        for (int u = 0; u < PASS; ++u) __builtin_amdgcn_raw_buffer_store_b128(vals[u], rsc, offs[u], 0, 2);  // nt
+      } else {
 #pragma unroll
-      for (int k = 0; k < NCH; ++k) __builtin_amdgcn_raw_buffer_store_b128(vals[k], rsc, offs[k], 0, 0);
+        for (int u = 0; u < PASS; ++u) __builtin_amdgcn_raw_buffer_store_b128(vals[u], rsc, offs[u], 0, 0);
+      }
     }
     if constexpr (AMAX) red[tid] = max(red[tid], omag);  // after the stores are issued
     __syncthreads();  // staging reads done before the next tile's copies land
@@ -734,7 +999,9 @@ template <int FA, int FB>
 void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, hipStream_t stream) {
   // skinny problems get their own launches; problems with few long tiles are
   // split along K when there is room for their partials; the rest share one
-  Batch rest{}, split{};
+  // (problems of fewer than four K blocks, which the 256 x 256 kernel's
+  // pipeline does not take, go to the smaller tiles in a launch of their own)
+  Batch rest{}, split{}, short_k{};
   const Problem *orig[kMaxGemms];
   size_t used = 0;
   for (int i = 0; i < b.count; ++i) {
@@ -752,6 +1019,8 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       q.bias = nullptr;
       q.amax_out = nullptr;  // taken by the reduce kernel
       used += need;
+    } else if (p.K < kMinBigK) {
+      short_k.p[short_k.count++] = p;
     } else {
       rest.p[rest.count++] = p;
     }
@@ -764,9 +1033,10 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       p.tiles_n = (p.N + 255) / 256;
       tiles += p.tiles_m * p.tiles_n * p.splits;
     }
-    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(split);
+    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 2, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 256, 0, stream>>>(split);
   }
-  if (rest.count > 0) {
+  auto launch_rest = [&](Batch &rest, bool big_ok) {
+    if (rest.count == 0) return;
     int64_t big = 0, small = 0;
     for (int i = 0; i < rest.count; ++i) {
       big += (int64_t)((rest.p[i].M + 255) / 256) * ((rest.p[i].N + 255) / 256);
@@ -785,7 +1055,7 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     // ones in three 43.0 us; 12288 x 4800 x 1600: four big rounds 99.4 us,
     // eight small ones 113 us).  A queued batch keeps the big tiles.
     const int64_t big_rounds = (big + kCUs - 1) / kCUs, small_rounds = (small + 2 * kCUs - 1) / (2 * kCUs);
-    const bool use_big = big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
+    const bool use_big = big_ok && big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
     // At most one small tile per CU (e.g. 256 tokens: 64 tiles of 128 x 128):
     // tiles of 64 x 128 occupy twice as many CUs (measured: 1024 x 4096 x
     // 4096, 256 small tiles, 25.8 -> 24.1 us; from 384 small tiles on the
@@ -809,7 +1079,7 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     if (use_big && mixed && queue && fixed_stride_unbalanced(rest, std::min(tiles, kCUs))) {
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;
-      launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_big && tiles >= 8 * kCUs) {
       // Eight or more rounds of tiles: groups of eight tile-rows, so that an
       // XCD's 32 concurrent tiles form an 8 x 4 patch instead of 4 x 8
@@ -817,15 +1087,17 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       // backward pair 1682 -> 1669 us; with one to four rounds the two
       // patches are level within noise, or 4 x 8 is ahead: 4096^3 57.7 vs
       // 58.3 us).
-      launch_tiled<FA, FB, 256, 256, 2, 4, 1, 8, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      launch_tiled<FA, FB, 256, 256, 2, 2, 1, 8, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_big) {
-      launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_med) {
       launch_tiled<FA, FB, 64, 128, 2, 2, 2, 8, false>(rest, (unsigned)std::min(tiles, 2 * kCUs), amax, stream);
     } else {
       launch_tiled<FA, FB, 128, 128, 2, 2, 2, 8, false>(rest, (unsigned)std::min(tiles, 2 * kCUs), amax, stream);
     }
-  }
+  };
+  launch_rest(rest, true);
+  launch_rest(short_k, false);
   for (int i = 0; i < split.count; ++i) {
     const Problem &q = split.p[i];
     const int64_t mn = (int64_t)q.M * q.N;

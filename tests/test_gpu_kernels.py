@@ -220,7 +220,13 @@ def _gemm_gpu(f8, a, fa, b, fb, inv_a, inv_b):
                                  (1024, 4096, 256),
                                  # more than eight rounds of 256x256 tiles (groups of eight tile-rows),
                                  # 129 x 17 tiles with ragged last rows and columns
-                                 (33008, 4144, 512)])
+                                 (33008, 4144, 512),
+                                 # 256x256 tiles, odd counts of K blocks (a virtual zero block in
+                                 # front): 5 whole, 5 with a ragged 80-byte block, 5 with a ragged
+                                 # 64-byte one (its zero half skipped), 13 whole; and 6 blocks with a
+                                 # ragged 64-byte one
+                                 (4096, 4096, 640), (8192, 4096, 592), (4096, 8192, 576), (4096, 4096, 1664),
+                                 (4096, 4096, 704)])
 def test_gemm_matches_oracle(f8, fa, fb, mnk):
     M, N, K = mnk
     print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
