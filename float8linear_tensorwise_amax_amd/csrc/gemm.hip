@@ -379,6 +379,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     auto mfma = [&](const v8i &a, const v8i &b, v16f &c) {
       c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
     };
+    // the same with the operands swapped: the 32 x 32 block of C^T, in which
+    // a lane holds four consecutive columns of one row of C
+    auto mfma_t = [&](const v8i &a, const v8i &b, v16f &c) {
+      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 0, 0, 0, 0);
+    };
     const int nk = (K + kBK - 1) / kBK;
     // A last K block with at most 64 bytes left (K = 1600, 4800) holds only
     // zeros in its second sub-step: those MFMAs would add exact zeros to
@@ -585,7 +590,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         const int ckb = (j + 5) >> 1;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-          mfma(fa2[P][H][t & 3], fb2[P][H][t >> 2], acc[t & 3][t >> 2]);
+          mfma_t(fa2[P][H][t & 3], fb2[P][H][t >> 2], acc[t & 3][t >> 2]);
           if (t == 1 && BAR) {
             if (vm >= 16)
               __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) lgkmcnt(0)
@@ -674,97 +679,155 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     }
 
     if constexpr (PARTIAL) {
-      // fp32 partial product, unscaled: lane (column c = lane & 31, half h)
-      // holds rows 8*(v>>2) + 4*h + (v&3) of each 32x32 tile; 32 lanes write
-      // 128 contiguous bytes of a row.  Rows past M lie outside the slab's
-      // range, columns past N get an offset outside it.
+      // fp32 partial product, unscaled: lane (row r = lane & 31, half h)
+      // holds, per 32x32 block, columns 8g + 4h .. +3 (g = 0..3) of row r
+      // (the MFMA ran on C^T): one 16-byte store each; rows past M lie
+      // outside the slab's range, columns past N get an offset outside it.
+      static_assert(kStag, "split problems take the 256 x 256 tiles");
       const int rows_c = min(BM, M - m0);
       const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(reinterpret_cast<float *>(P.c) + ((int64_t)range * M + m0) * N), (short)0, rows_c * N * 4,
           0x00020000);
-      // (with 256 x 256 tiles the lane index is regenerated here: the
-      // addresses are derived per tile, not kept across the K loop)
-      const int pl = kStag ? lane_here() : lane;
+      // (the lane index regenerated here: the addresses are derived per
+      // tile, not kept across the K loop)
+      const int pl = lane_here();
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm + i * 32 + (pl & 31);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn + j * 32 + (pl & 31);
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (pl >> 5) + (v & 3);
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + wn + j * 32 + 8 * g + 4 * (pl >> 5);
             const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rsp, vo, 0, 0);
+            const u32x4 v{__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
+                          __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsp, vo, 0, 0);
           }
-        }
+      }
       __syncthreads();  // every wave is done with the stage buffers before the next tile's copies
       it += wx;
       continue;
     }
 
-    // Epilogue.  Lane (column c = lane & 31, half h = lane >> 5) holds, per
-    // 32x32 tile, rows 8*(v>>2) + 4*h + (v&3) for v = 0..15.  Even lanes take
-    // column pair (c, c+1) at even v, odd lanes (c-1, c) at odd v: each lane
-    // keeps one of its values v = 2k, 2k+1 and sends the other to the
-    // neighbour lane (a DPP swap folded into the scaling multiply); the pair,
-    // rounded to bf16 as (kept, received), is one 32-bit LDS word, its halves
-    // swapped on odd lanes (a rotate by a per-lane amount).  Rows of even /
-    // odd v differ in parity and rows of the two halves in bit 2 (stage_swz
-    // moves them to other banks), so each write is free of bank conflicts.
+    // Epilogue: the tile, scaled (+ bias) and rounded to bf16, is staged in
+    // LDS row by row per wave, then read back in 16-byte row chunks and
+    // stored.
     __syncthreads();  // every wave is done with the stage buffers
     const float alpha = inv_a * inv_b;
     // The lane index of the epilogue: with 256 x 256 tiles regenerated here,
     // so that the compiler derives the epilogue's addresses from it per tile
     // instead of keeping them (spilled) across the K loop.
     const int el = kStag ? lane_here() : lane;
-    // byte swizzle of a staged row: rows with bit 2 set swap their 64-byte
-    // halves; 256-byte rows (one full set of banks) also swap the 128-byte
-    // halves of odd rows, which the other lane of a column pair writes
-    auto stage_swz = [](int row) { return (((row >> 2) & 1) << 6) ^ (RB >= 256 ? (row & 1) << 7 : 0); };
     uint8_t *wreg = smem + wave * (WTM * RB);
-    const bool odd = el & 1;
-    const uint32_t rot = odd ? 16u : 0u;
-    auto stage_out = [&](auto BIAS) {
-      // bias of the kept and the received value of this lane's column pair
-      // (cpair, cpair + 1) of each 32-column tile j
-      float bias_keep[TN], bias_recv[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        bias_keep[j] = bias_recv[j] = 0.0f;
-        if constexpr (decltype(BIAS)::value) {
-          const int gc = n0 + wn + j * 32 + (el & 30);
-          const uint32_t bw = gc < N ? *(const uint32_t *)(P.bias + gc) : 0u;
-          const float lo = __uint_as_float(bw << 16), hi = __uint_as_float(bw & 0xFFFF0000u);
-          bias_keep[j] = odd ? hi : lo;
-          bias_recv[j] = odd ? lo : hi;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
+    // Staged row r, 16-byte chunk ch: at wreg + r * RB + chunk_at(r, ch),
+    // with the chunk's two 8-byte halves swapped when half_swap(r).
+    //  * 256 x 256 tiles (RB = 256, one full set of banks): the MFMA ran on
+    //    C^T, so lane (row r = lane & 31 of each 32x32 block, half h = lane
+    //    >> 5) holds, for g = 0..3, columns 8g + 4h .. +3 of row r: 8 bytes of
+    //    bf16, the half h of chunk 4j + g.  Chunks are XOR-ed with r & 15 and
+    //    the halves swapped on rows with bit 4 set, so the 32 lanes of either
+    //    half of a wave write 32 distinct 8-byte slots of the 256 banks' row.
+    //  * smaller tiles (RB = 128): lane (column c = lane & 31, half h) holds
+    //    rows 8*(v>>2) + 4*h + (v&3) for v = 0..15.  Even lanes take column
+    //    pair (c, c+1) at even v, odd lanes (c-1, c) at odd v: each lane keeps
+    //    one of its values v = 2k, 2k+1 and sends the other to the neighbour
+    //    lane (a DPP swap folded into the scaling multiply); the pair, rounded
+    //    to bf16 as (kept, received), is one 32-bit LDS word, its halves
+    //    swapped on odd lanes (a rotate by a per-lane amount).  Rows of even /
+    //    odd v differ in parity and rows of the two halves in bit 2 (which
+    //    swaps the 64-byte halves of the row), so each write is free of bank
+    //    conflicts.
+    auto chunk_at = [](int row, int ch) {
+      return kStag ? ((ch ^ (row & 15)) << 4) : ((ch * 16) ^ (((row >> 2) & 1) << 6));
+    };
+    if constexpr (kStag) {
+      static_assert(RB == 256 && TM == 4 && TN == 4, "staging of the 256 x 256 tiles");
+      const int l = el & 31, h = el >> 5;
+      auto stage_t = [&](auto BIAS) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int cpair = j * 32 + (el & 30);
+          // bias of this lane's four columns of each group g (bf16 words)
+          u32x2 bw[4];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
-            const float keep = odd ? a1 : a0, send = odd ? a0 : a1;
-            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
-            float ks = keep * alpha, rs = recv * alpha;
+          for (int g = 0; g < 4; ++g) {
+            bw[g] = u32x2{0u, 0u};
             if constexpr (decltype(BIAS)::value) {
-              ks += bias_keep[j];
-              rs += bias_recv[j];
+              const int gc = n0 + wn + j * 32 + 8 * g + 4 * h;
+              if (gc < N) bw[g] = *(const u32x2 *)(P.bias + gc);
             }
-            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ks, rs}, bf16x2));
-            const int v = 2 * k + (odd ? 1 : 0);
-            const int row = i * 32 + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
-            *(uint32_t *)(wreg + row * RB + ((cpair * 2) ^ stage_swz(row))) = __builtin_amdgcn_alignbit(w, w, rot);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const int row = i * 32 + l;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              float x0 = acc[i][j][4 * g] * alpha, x1 = acc[i][j][4 * g + 1] * alpha;
+              float x2 = acc[i][j][4 * g + 2] * alpha, x3 = acc[i][j][4 * g + 3] * alpha;
+              if constexpr (decltype(BIAS)::value) {
+                x0 += __uint_as_float(bw[g].x << 16);
+                x1 += __uint_as_float(bw[g].x & 0xFFFF0000u);
+                x2 += __uint_as_float(bw[g].y << 16);
+                x3 += __uint_as_float(bw[g].y & 0xFFFF0000u);
+              }
+              const u32x2 w{__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2)),
+                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x2, x3}, bf16x2))};
+              const int half = h ^ ((row >> 4) & 1);
+              *(u32x2 *)(wreg + row * RB + chunk_at(row, 4 * j + g) + 8 * half) = w;
+            }
           }
         }
-    };
-    if (P.bias)
-      stage_out(bool_t<true>());
-    else
-      stage_out(bool_t<false>());
+      };
+      if (P.bias)
+        stage_t(bool_t<true>());
+      else
+        stage_t(bool_t<false>());
+    } else {
+      const bool odd = el & 1;
+      const uint32_t rot = odd ? 16u : 0u;
+      auto stage_out = [&](auto BIAS) {
+        // bias of the kept and the received value of this lane's column pair
+        // (cpair, cpair + 1) of each 32-column tile j
+        float bias_keep[TN], bias_recv[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          bias_keep[j] = bias_recv[j] = 0.0f;
+          if constexpr (decltype(BIAS)::value) {
+            const int gc = n0 + wn + j * 32 + (el & 30);
+            const uint32_t bw = gc < N ? *(const uint32_t *)(P.bias + gc) : 0u;
+            const float lo = __uint_as_float(bw << 16), hi = __uint_as_float(bw & 0xFFFF0000u);
+            bias_keep[j] = odd ? hi : lo;
+            bias_recv[j] = odd ? lo : hi;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int cpair = j * 32 + (el & 30);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float a0 = acc[i][j][2 * k], a1 = acc[i][j][2 * k + 1];
+              const float keep = odd ? a1 : a0, send = odd ? a0 : a1;
+              const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+              float ks = keep * alpha, rs = recv * alpha;
+              if constexpr (decltype(BIAS)::value) {
+                ks += bias_keep[j];
+                rs += bias_recv[j];
+              }
+              const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ks, rs}, bf16x2));
+              const int v = 2 * k + (odd ? 1 : 0);
+              const int row = i * 32 + 8 * (v >> 2) + 4 * (el >> 5) + (v & 3);
+              *(uint32_t *)(wreg + row * RB + ((cpair * 2) ^ (((row >> 2) & 1) << 6))) =
+                  __builtin_amdgcn_alignbit(w, w, rot);
+            }
+          }
+      };
+      if (P.bias)
+        stage_out(bool_t<true>());
+      else
+        stage_out(bool_t<false>());
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
     // All of the wave's staged chunks are read first, then stored with
@@ -787,7 +850,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (int u = 0; u < PASS; ++u) {
         const int idx = (k0 + u) * 64 + el;
         const int row = idx / CPR, ch = idx % CPR;
-        vals[u] = *(const u32x4 *)(wreg + row * RB + ((ch * 16) ^ stage_swz(row)));
+        vals[u] = *(const u32x4 *)(wreg + row * RB + chunk_at(row, ch));
+        // (with 256 x 256 tiles, the rows of one read share bit 4: row =
+        // 4 (k0 + u) + (lane >> 4), so the half swap is known here)
+        if constexpr (kStag)
+          if (((k0 + u) >> 2) & 1) vals[u] = u32x4{vals[u].z, vals[u].w, vals[u].x, vals[u].y};
         const int gcol = n0 + wn + ch * 8;
         offs[u] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
         if constexpr (AMAX) {
