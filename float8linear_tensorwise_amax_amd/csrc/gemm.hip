@@ -90,6 +90,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
 constexpr int kMinBigK = 4 * kBK;  // shortest K the 256 x 256 tiles take
+#ifndef F8LIN_SPLIT_STAG_BLOCKS
+#define F8LIN_SPLIT_STAG_BLOCKS 16
+#endif
+constexpr int kSplitStagBlocks = F8LIN_SPLIT_STAG_BLOCKS;  // shortest split range the four-wave tiles take
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 // Every matrix dimension is at most 2^22 (checked at the C ABI), so a tile's
@@ -679,30 +683,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     }
 
     if constexpr (PARTIAL) {
-      // fp32 partial product, unscaled: lane (row r = lane & 31, half h)
-      // holds, per 32x32 block, columns 8g + 4h .. +3 (g = 0..3) of row r
-      // (the MFMA ran on C^T): one 16-byte store each; rows past M lie
-      // outside the slab's range, columns past N get an offset outside it.
-      static_assert(kStag, "split problems take the 256 x 256 tiles");
       const int rows_c = min(BM, M - m0);
       const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(reinterpret_cast<float *>(P.c) + ((int64_t)range * M + m0) * N), (short)0, rows_c * N * 4,
           0x00020000);
-      // (the lane index regenerated here: the addresses are derived per
-      // tile, not kept across the K loop)
-      const int pl = lane_here();
+      // (the lane index regenerated here with the four-wave tiles: the
+      // addresses are derived per tile, not kept across the K loop)
+      const int pl = kStag ? lane_here() : lane;
+      if constexpr (kStag) {
+        // fp32 partial product, unscaled: lane (row r = lane & 31, half h)
+        // holds, per 32x32 block, columns 8g + 4h .. +3 (g = 0..3) of row r
+        // (the MFMA ran on C^T): one 16-byte store each; rows past M lie
+        // outside the slab's range, columns past N get an offset outside it.
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm + i * 32 + (pl & 31);
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm + i * 32 + (pl & 31);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn + j * 32 + 8 * g + 4 * (pl >> 5);
-            const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
-            const u32x4 v{__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
-                          __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3])};
-            __builtin_amdgcn_raw_buffer_store_b128(v, rsp, vo, 0, 0);
+            for (int g = 0; g < 4; ++g) {
+              const int col = n0 + wn + j * 32 + 8 * g + 4 * (pl >> 5);
+              const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
+              const u32x4 v{__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
+                            __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3])};
+              __builtin_amdgcn_raw_buffer_store_b128(v, rsp, vo, 0, 0);
+            }
+        }
+      } else {
+        // lane (column c = lane & 31, half h) holds rows 8*(v>>2) + 4*h +
+        // (v&3) of each 32x32 tile; 32 lanes write 128 contiguous bytes of a
+        // row
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn + j * 32 + (pl & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int row = wm + i * 32 + 8 * (v >> 2) + 4 * (pl >> 5) + (v & 3);
+              const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rsp, vo, 0, 0);
+            }
           }
       }
       __syncthreads();  // every wave is done with the stage buffers before the next tile's copies
@@ -1066,8 +1087,8 @@ template <int FA, int FB>
 void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, hipStream_t stream) {
   // skinny problems get their own launches; problems with few long tiles are
   // split along K when there is room for their partials; the rest share one
-  // (problems of fewer than four K blocks, which the 256 x 256 kernel's
-  // pipeline does not take, go to the smaller tiles in a launch of their own)
+  // (problems of fewer than four K blocks, which the four-wave 256 x 256
+  // kernel's pipeline does not take, go to a launch of their own)
   Batch rest{}, split{}, short_k{};
   const Problem *orig[kMaxGemms];
   size_t used = 0;
@@ -1100,9 +1121,20 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       p.tiles_n = (p.N + 255) / 256;
       tiles += p.tiles_m * p.tiles_n * p.splits;
     }
-    gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 2, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 256, 0, stream>>>(split);
+    // short ranges take the eight-wave tiles (their per-tile prologue and
+    // epilogue overlap between the two waves of a SIMD)
+    int min_blocks = 1 << 30;
+    for (int i = 0; i < split.count; ++i)
+      min_blocks = std::min(min_blocks, ((split.p[i].K + kBK - 1) / kBK) / split.p[i].splits);
+    if (min_blocks >= kSplitStagBlocks)
+      gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 2, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 256, 0, stream>>>(split);
+    else
+      gemm_fp8_tn_kernel<FA, FB, 256, 256, 2, 4, 1, 4, true><<<(unsigned)std::min(tiles, kCUs), 512, 0, stream>>>(split);
   }
-  auto launch_rest = [&](Batch &rest, bool big_ok) {
+  // stag: 256 x 256 tiles take the four-wave kernel (at least four K
+  // blocks), else the eight-wave one (2 x 4 waves of 128 x 64, two per SIMD,
+  // the K loop of the smaller tiles)
+  auto launch_rest = [&](Batch &rest, bool stag) {
     if (rest.count == 0) return;
     int64_t big = 0, small = 0;
     for (int i = 0; i < rest.count; ++i) {
@@ -1122,7 +1154,7 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     // ones in three 43.0 us; 12288 x 4800 x 1600: four big rounds 99.4 us,
     // eight small ones 113 us).  A queued batch keeps the big tiles.
     const int64_t big_rounds = (big + kCUs - 1) / kCUs, small_rounds = (small + 2 * kCUs - 1) / (2 * kCUs);
-    const bool use_big = big_ok && big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
+    const bool use_big = big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
     // At most one small tile per CU (e.g. 256 tokens: 64 tiles of 128 x 128):
     // tiles of 64 x 128 occupy twice as many CUs (measured: 1024 x 4096 x
     // 4096, 256 small tiles, 25.8 -> 24.1 us; from 384 small tiles on the
@@ -1146,7 +1178,10 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     if (use_big && mixed && queue && fixed_stride_unbalanced(rest, std::min(tiles, kCUs))) {
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;
-      launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      if (stag)
+        launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      else
+        launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, true>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_big && tiles >= 8 * kCUs) {
       // Eight or more rounds of tiles: groups of eight tile-rows, so that an
       // XCD's 32 concurrent tiles form an 8 x 4 patch instead of 4 x 8
@@ -1154,9 +1189,15 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       // backward pair 1682 -> 1669 us; with one to four rounds the two
       // patches are level within noise, or 4 x 8 is ahead: 4096^3 57.7 vs
       // 58.3 us).
-      launch_tiled<FA, FB, 256, 256, 2, 2, 1, 8, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      if (stag)
+        launch_tiled<FA, FB, 256, 256, 2, 2, 1, 8, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      else
+        launch_tiled<FA, FB, 256, 256, 2, 4, 1, 8, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_big) {
-      launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      if (stag)
+        launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
+      else
+        launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, false>(rest, (unsigned)std::min(tiles, kCUs), amax, stream);
     } else if (use_med) {
       launch_tiled<FA, FB, 64, 128, 2, 2, 2, 8, false>(rest, (unsigned)std::min(tiles, 2 * kCUs), amax, stream);
     } else {
