@@ -9,15 +9,22 @@
 // input); problems with M <= 64 take a skinny kernel of their own (below).
 //
 // gfx950 design (each choice measured on MI355X):
-//   * v_mfma_f32_32x32x64_f8f6f4 (the scaled builtin with zero scale operands
-//     selects the unscaled instruction); e4m3 / e5m2 per operand through
-//     cbsz / blgp.  A lane feeds the same 32 K-bytes of its A row and of its
-//     B row, so A and B share one K order and the instruction's internal K
-//     order cannot matter.
+//   * v_mfma_f32_16x16x128_f8f6f4 in the big tiles, v_mfma_f32_32x32x64_f8f6f4
+//     in the others (the scaled builtins with zero scale operands select the
+//     unscaled instructions); e4m3 / e5m2 per operand through cbsz / blgp.
+//     A lane feeds the same 32 K-bytes of its A row and of its B row, so A
+//     and B share one K order and the instruction's internal K order cannot
+//     matter.  The matrix cores are power-bound on real data: on random fp8
+//     codes from registers the 16 x 16 x 128 instruction runs ~10% more
+//     flops per second than the 32 x 32 x 64 one (the chip holds ~2.04
+//     instead of ~1.89 GHz): it moves half the accumulator data per flop.
 //   * Workgroups:
 //       big   256 x 256 tile, 4 waves (2 x 2, one per SIMD), wave tile
 //             128 x 128 (256 fp32 accumulators per lane, in the AGPRs), one
-//             workgroup per CU, with its own K loop (below);
+//             workgroup per CU, with its own K loop (below); contractions
+//             of fewer than four K blocks and split-K ranges of fewer than
+//             16 take 8 waves instead (2 x 4, wave tile 128 x 64, two per
+//             SIMD, the loop of the smaller tiles);
 //       small 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64, two per CU,
 //             for problems with too few big tiles to fill 256 CUs, or
 //             whose ragged edge would leave the last round of big tiles
@@ -44,15 +51,17 @@
 //     and retires block k, whose buffer then receives block k+2; those copies
 //     are spread between the MFMAs that follow.
 //   * The big tile's K loop (one wave per SIMD, so nothing hides a wave's
-//     stall but its own schedule): each block's A fragments (both K halves)
-//     are read from LDS in one 16-MFMA step and its B fragments in the next,
-//     so the A and B regions of a stage are freed one step apart and each
-//     step refills one region: every step issues the same eighth of a
-//     block's copies, and a copy has two to three steps to land before it is
-//     read (the fragments of three half-blocks, 192 VGPRs, are held).  On
-//     4096 x 4096 x 16384 this keeps the matrix cores ~89-95% busy against
-//     ~83% for two waves per SIMD with a 128 x 64 wave tile, which read
-//     1.5x the LDS bytes per flop.
+//     stall but its own schedule): each block's A fragments are read from
+//     LDS during one 32-MFMA step and its B fragments during the next, so the
+//     A and B regions of a stage are freed one step apart and each step
+//     refills one region (eight 1 KB copies per wave): every step issues the
+//     same share of copies, and a copy has two to three steps to land before
+//     it is read.  A fragment is mostly read into the registers of the one it
+//     replaces right after that one's last MFMA, so ~22 of them (176 VGPRs)
+//     are live.  On 4096 x 4096 x 16384 this runs 6% faster than the same
+//     loop on 32 x 32 x 64 MFMAs (same box).  Two waves per SIMD with a
+//     128 x 64 wave tile read 1.5x the LDS bytes per flop and were slower
+//     still.
 //   * The matrix cores and the memory system together exceed the chip's power
 //     budget: the shader clock drops from 2.4 GHz to ~1.7-2.0 GHz while this
 //     loop runs (read with s_memtime against the constant-rate counter), so
@@ -380,13 +389,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // (256 x 256 tiles of four waves: 8 x 8 blocks of 16 x 16 instead)
+    v4f acc4[kStag ? 8 : 1][kStag ? 8 : 1];
+    if constexpr (kStag) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc4[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     auto mfma = [&](const v8i &a, const v8i &b, v16f &c) {
       c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
-    };
-    // the same with the operands swapped: the 32 x 32 block of C^T, in which
-    // a lane holds four consecutive columns of one row of C
-    auto mfma_t = [&](const v8i &a, const v8i &b, v16f &c) {
-      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 0, 0, 0, 0);
     };
     const int nk = (K + kBK - 1) / kBK;
     // A last K block with at most 64 bytes left (K = 1600, 4800) holds only
@@ -477,23 +489,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         publish();
       }
     } else {
-      // Four waves of 128 x 128 (one per SIMD).  A region is one operand of
-      // one K block: region 2 kb + X (X = 0: A, 1: B); consecutive blocks
-      // alternate between the two stages.
-      // Step j = 2 s + h runs the 16 MFMAs of K block s, half h, from
-      // registers; meanwhile it reads all fragments of region j + 2 (both
-      // halves of one operand of block s + 1) and copies region j + 5 over
-      // region j + 1, which step j - 1 finished reading.  So every step
-      // issues the same share of copies, and a copy has two to three steps to
-      // land before its region is read; the fragments of three half-blocks
-      // are held in registers.  The barrier of step j sits after its second
-      // MFMA: each wave has then finished the reads of step j - 1 and
-      // received all its copies of region j + 2.
+      // Four waves of 128 x 128 (one per SIMD), v_mfma_f32_16x16x128_f8f6f4
+      // on C^T: 8 x 8 accumulator blocks of 16 x 16, and a fragment is 16
+      // rows of one operand over a whole K block (lane l: row l & 15, K
+      // bytes 32 (l >> 4) .. +32).  (Per flop it moves half the accumulator
+      // data of the 32 x 32 x 64 instruction; on random codes the chip then
+      // holds a ~8% higher clock.)  A region is one operand of one K block:
+      // region 2 kb + X (X = 0: A, 1: B); consecutive blocks alternate
+      // between the two stages.
+      // Step j = 2 s + h runs 32 MFMAs of K block s from registers: A
+      // fragments 4h .. 4h + 3 against all eight B fragments (h = 0: A
+      // fragment by fragment; h = 1: B fragment by fragment).  Meanwhile it
+      // reads all fragments of region j + 2 (one operand of block s + 1) and
+      // copies region j + 5 over region j + 1, which step j - 1 finished
+      // reading.  So every step issues the same share of copies, and a copy
+      // has two to three steps to land before its region is read.  A
+      // fragment of block s + 1 is mostly read right after the fragment of
+      // block s it replaces has had its last MFMA, so at most ~22 fragments
+      // are live.  The barrier of step j sits after its fourth MFMA: each
+      // wave has then finished the reads of step j - 1 and received all its
+      // copies of region j + 2.
       static_assert(TM == 4 && TN == 4 && LA == 8 && LB == 8 && OPA == OPB, "four 128 x 128 wave tiles");
-      // An odd count of K blocks gets a virtual block at the end (its copies
-      // re-read a real block, its two steps -- MFMAs only -- are skipped), so
-      // that the pipeline always runs an even count nkp and one sequence of
-      // steps.
+      // An odd count of K blocks gets a virtual block at the end, so that
+      // the pipeline always runs an even count nkp and one sequence of steps
+      // with no branch: its copies fetch zeros, and its two steps (MFMAs only)
+      // add exact zeros to accumulators that can never hold -0 (same bits).
       const int virt = nkb & 1, nkp = nkb + virt;
       const int swave = wave;  // (a scalar here)
       // lane-derived addresses are computed per tile from a regenerated lane
@@ -505,25 +525,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       // below 64 KB (four bases per operand).
       auto region = [&](int S, int X) { return smem + X * 2 * OPA + S * OPA; };
       // Byte offset, within a region, of this lane's 16-byte chunk lo (0/1)
-      // of K half hh in fragment 0 of operand X: row r = w + l (w the wave's
-      // first row, a multiple of 16; l = lane & 31), chunk c = 4 hh + 2 (lane
-      // >> 5) + lo, at slot128(r, c); fragment f is 32 rows (4096 bytes) on.
-      int rdb[2][2][2];
+      // in fragment 0 of operand X: row r = w + l (w the wave's first row, a
+      // multiple of 16; l = lane & 15), chunk c = 2 (lane >> 4) + lo, at
+      // slot128(r, c); fragment f is 16 rows (2048 bytes) on.
+      int rdb[2][2];
 #pragma unroll
       for (int X = 0; X < 2; ++X)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int lo = 0; lo < 2; ++lo) {
-            const int l = kl & 31, c = hh * 4 + (kl >> 5) * 2 + lo;
-            rdb[X][hh][lo] = ((X ? wn : wm) + l) * 128 + ((c ^ ((l >> 1) & 7)) << 4);
-          }
-      auto rd2 = [&](int S, int X, int f, int hh) {
-        const uint8_t *st = region(S, X) + f * 4096;
-        const u32x4 lo = *(const u32x4 *)(st + rdb[X][hh][0]), hi = *(const u32x4 *)(st + rdb[X][hh][1]);
+        for (int lo = 0; lo < 2; ++lo) {
+          const int l = kl & 15, c = (kl >> 4) * 2 + lo;
+          rdb[X][lo] = ((X ? wn : wm) + l) * 128 + ((c ^ ((l >> 1) & 7)) << 4);
+        }
+      auto rd16 = [&](int S, int X, int f) {
+        const uint8_t *st = region(S, X) + f * 2048;
+        const u32x4 lo = *(const u32x4 *)(st + rdb[X][0]), hi = *(const u32x4 *)(st + rdb[X][1]);
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       };
-      v8i fa2[2][2][TM], fb2[2][2][TN];  // [block parity][K half][fragment]
+      v8i fa[2][8], fb[2][8];  // [block parity][fragment]
       // Copy q's slots (LA = 8) start 16 (q >> 1) rows past those of copy
       // q & 1: its global offset is one of two per-lane bases plus a uniform
       // row step, and its K byte the base's chunk.
@@ -542,9 +560,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       // Copy q of region (X, pipeline block kb) into stage S.  The row stays
       // in the per-lane offset (rows past the tile fail the range check) and
       // the block's K offset rides in the scalar offset.  MODE 0: a whole
-      // block (or the virtual one); 1: a block of the prologue, which may be
-      // the ragged one (lanes whose 16 bytes start at or past K out of range,
-      // which loads zeros: K is a multiple of 16).
+      // block; 2: the last pipeline block (all lanes out of range when it is
+      // the virtual one, which loads zeros); 1: a block of the prologue, which
+      // may be the ragged one (lanes whose 16 bytes start at or past K out of
+      // range: K is a multiple of 16).
       // The K byte offset of pipeline block kb >= 1 is linear in kb (kept in
       // scalar registers): forward from -ragged blocks, or backward from nkb - 1
       // (odd tile bands); clamped to the whole blocks for the virtual one.
@@ -567,6 +586,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         if constexpr (MODE == 0) {
           const int k0 = min(max(k00 + kb * kstep, 0), kmax);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? rsa : rsb, dst, 16, vrow, k0, 0, 0);
+        } else if constexpr (MODE == 2) {
+          const int k0 = min(max(k00 + kb * kstep, 0), kmax);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(X == 0 ? rsa : rsb, dst, 16, virt ? kOutOfRange : vrow, k0, 0, 0);
         } else {
           const int kp = rev ? nkb - 1 - kb : (ragged ? (kb == 0 ? nkb - 1 : kb - 1) : kb);
           const int k0 = kp * kBK;
@@ -579,10 +601,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
 #pragma unroll
         for (int q = 0; q < LA; ++q) copy_region(X_, S_, int_t<1>(), kb, q);
       };
-      // MFMA slots of a step's fragment reads (half 0 fragments 0-3, then
-      // half 1) and copies, after the barrier
-      constexpr int kRdSlot[16] = {-1, -1, 0, 1, 2, -1, 3, 4, -1, 5, 6, -1, 7, -1, -1, -1};
-      constexpr int kCpSlot[16] = {-1, -1, 0, -1, 1, -1, 2, -1, 3, -1, 4, -1, 5, 6, -1, 7};
+      // The fragment read and the copy issued after each MFMA slot of a step
+      // (all after the barrier at slot 3).  A step (h = 0): the next block's
+      // A fragments 4-7 at once, then 0-3 as the current fragments 0, 1, 2
+      // have their last MFMAs (slots 7, 15, 23).  B step (h = 1): next
+      // fragment f after the current one's last MFMA (slot 4 f + 3), 5-7 a
+      // little early, so that the last read is eight MFMAs ahead of its use.
+      constexpr int kRdA[32] = {-1, -1, -1, -1, 4,  5,  6,  7,  0,  -1, -1, -1, 1,  -1, -1, -1,
+                                2,  -1, -1, -1, 3,  -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+      constexpr int kRdB[32] = {-1, -1, -1, -1, 0,  -1, -1, -1, 1,  -1, -1, -1, 2,  -1, -1, -1,
+                                3,  -1, -1, -1, 4,  -1, 5,  6,  7,  -1, -1, -1, -1, -1, -1, -1};
+      constexpr int kCp[32] = {-1, -1, -1, -1, -1, -1, 0,  -1, -1, 1,  -1, -1, -1, 2,  -1, -1,
+                               -1, 3,  -1, -1, -1, 4,  -1, -1, -1, 5,  -1, 6,  -1, 7,  -1, -1};
+      auto mfma16 = [&](const v8i &a, const v8i &b, v4f &c) {
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, FB, FA, 0, 0, 0, 0);
+      };
       // step j (block parity P, half H); RD / CP: whether region j + 2 / j + 5
       // exist; MODE: the copies' kind; VM: copies of this wave that may still
       // be in flight at the barrier (those of regions j + 3 and j + 4 that
@@ -593,9 +626,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         constexpr int RP = P ^ 1, CS = H == 0 ? P : P ^ 1;
         const int ckb = (j + 5) >> 1;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          mfma_t(fa2[P][H][t & 3], fb2[P][H][t >> 2], acc[t & 3][t >> 2]);
-          if (t == 1 && BAR) {
+        for (int t = 0; t < 32; ++t) {
+          {
+            const int i = H == 0 ? t >> 3 : 4 + (t & 3), jj = H == 0 ? t & 7 : t >> 2;
+            mfma16(fa[P][i], fb[P][jj], acc4[i][jj]);
+          }
+          if (t == 3 && BAR) {
             if (vm >= 16)
               __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) lgkmcnt(0)
             else if (vm >= 8)
@@ -604,14 +640,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
               __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
           }
-          if (RD && kRdSlot[t] >= 0) {
-            const int f = kRdSlot[t] & 3, hh = kRdSlot[t] >> 2;
-            if constexpr (H == 0)
-              fa2[RP][hh][f] = rd2(RP, 0, f, hh);
-            else
-              fb2[RP][hh][f] = rd2(RP, 1, f, hh);
+          if constexpr (H == 0) {
+            if (RD && kRdA[t] >= 0) fa[RP][kRdA[t]] = rd16(RP, 0, kRdA[t]);
+          } else {
+            if (RD && kRdB[t] >= 0) fb[RP][kRdB[t]] = rd16(RP, 1, kRdB[t]);
           }
-          if (CP && kCpSlot[t] >= 0) copy_region(int_t<H ^ 1>(), int_t<CS>(), MODE, ckb, kCpSlot[t]);
+          if (CP && kCp[t] >= 0) copy_region(int_t<H ^ 1>(), int_t<CS>(), MODE, ckb, kCp[t]);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -624,10 +658,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       auto tstep = [&](auto D_, auto P_, auto H_, int j) {
         constexpr int d = decltype(D_)::value;
         if constexpr (d >= 2) {
-          step(P_, H_, T, bool_t<(d >= 5)>(), int_t<0>(), T, d >= 4 ? 16 : (d == 3 ? 8 : 0), j);
+          step(P_, H_, T, bool_t<(d >= 5)>(), int_t<2>(), T, d >= 4 ? 16 : (d == 3 ? 8 : 0), j);
         } else {
-          // the last block: MFMAs only; skipped whole when it is the virtual one
-          if (!virt) step(P_, H_, bool_t<false>(), bool_t<false>(), int_t<0>(), bool_t<false>(), 0, j);
+          // the last block: MFMAs only
+          step(P_, H_, bool_t<false>(), bool_t<false>(), int_t<0>(), bool_t<false>(), 0, j);
         }
       };
       // steps j .. j + D0 (d = D0 .. 0), the first of parity (P0, H0)
@@ -654,12 +688,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       __builtin_amdgcn_s_barrier();
       publish();
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          fa2[0][hh][f] = rd2(0, 0, f, hh);
-          fb2[0][hh][f] = rd2(0, 1, f, hh);
-        }
+      for (int f = 0; f < 8; ++f) {
+        fa[0][f] = rd16(0, 0, f);
+        fb[0][f] = rd16(0, 1, f);
+      }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): block 0 read by this wave
       __builtin_amdgcn_s_barrier();         // ... and by all
       copy_all(int_t<0>(), int_t<0>(), 2);
@@ -691,23 +723,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       // addresses are derived per tile, not kept across the K loop)
       const int pl = kStag ? lane_here() : lane;
       if constexpr (kStag) {
-        // fp32 partial product, unscaled: lane (row r = lane & 31, half h)
-        // holds, per 32x32 block, columns 8g + 4h .. +3 (g = 0..3) of row r
-        // (the MFMA ran on C^T): one 16-byte store each; rows past M lie
-        // outside the slab's range, columns past N get an offset outside it.
+        // fp32 partial product, unscaled: lane (row r = lane & 15, quarter q
+        // = lane >> 4) holds columns 4q .. 4q + 3 of row r of each 16 x 16
+        // block (the MFMA ran on C^T): one 16-byte store each; rows past M
+        // lie outside the slab's range, columns past N get an offset outside
+        // it.
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = wm + i * 32 + (pl & 31);
+        for (int i = 0; i < 8; ++i) {
+          const int row = wm + i * 16 + (pl & 15);
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int col = n0 + wn + j * 32 + 8 * g + 4 * (pl >> 5);
-              const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
-              const u32x4 v{__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
-                            __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3])};
-              __builtin_amdgcn_raw_buffer_store_b128(v, rsp, vo, 0, 0);
-            }
+          for (int j = 0; j < 8; ++j) {
+            const int col = n0 + wn + j * 16 + 4 * (pl >> 4);
+            const int vo = col < N ? (row * N + col) * 4 : kOutOfRange;
+            const u32x4 v{__float_as_uint(acc4[i][j][0]), __float_as_uint(acc4[i][j][1]),
+                          __float_as_uint(acc4[i][j][2]), __float_as_uint(acc4[i][j][3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsp, vo, 0, 0);
+          }
         }
       } else {
         // lane (column c = lane & 31, half h) holds rows 8*(v>>2) + 4*h +
@@ -741,14 +772,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     // instead of keeping them (spilled) across the K loop.
     const int el = kStag ? lane_here() : lane;
     uint8_t *wreg = smem + wave * (WTM * RB);
-    // Staged row r, 16-byte chunk ch: at wreg + r * RB + chunk_at(r, ch),
-    // with the chunk's two 8-byte halves swapped when half_swap(r).
+    // Staged row r, 16-byte chunk ch: at wreg + r * RB + chunk_at(r, ch).
     //  * 256 x 256 tiles (RB = 256, one full set of banks): the MFMA ran on
-    //    C^T, so lane (row r = lane & 31 of each 32x32 block, half h = lane
-    //    >> 5) holds, for g = 0..3, columns 8g + 4h .. +3 of row r: 8 bytes of
-    //    bf16, the half h of chunk 4j + g.  Chunks are XOR-ed with r & 15 and
-    //    the halves swapped on rows with bit 4 set, so the 32 lanes of either
-    //    half of a wave write 32 distinct 8-byte slots of the 256 banks' row.
+    //    C^T, so lane (row r = lane & 15 of each 16 x 16 block (i, j),
+    //    quarter q = lane >> 4) holds columns 4q .. 4q + 3 of row r: 8 bytes
+    //    of bf16, half q & 1 of chunk 2j + (q >> 1).  Chunks are XOR-ed with
+    //    r, so the 32 lanes of either half of a wave write 32 distinct 8-byte
+    //    slots of the 256 banks' row.
     //  * smaller tiles (RB = 128): lane (column c = lane & 31, half h) holds
     //    rows 8*(v>>2) + 4*h + (v&3) for v = 0..15.  Even lanes take column
     //    pair (c, c+1) at even v, odd lanes (c-1, c) at odd v: each lane keeps
@@ -763,39 +793,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       return kStag ? ((ch ^ (row & 15)) << 4) : ((ch * 16) ^ (((row >> 2) & 1) << 6));
     };
     if constexpr (kStag) {
-      static_assert(RB == 256 && TM == 4 && TN == 4, "staging of the 256 x 256 tiles");
-      const int l = el & 31, h = el >> 5;
+      static_assert(RB == 256, "staging of the 256 x 256 tiles");
+      const int r = el & 15, q = el >> 4;
       auto stage_t = [&](auto BIAS) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          // bias of this lane's four columns of each group g (bf16 words)
-          u32x2 bw[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bw[g] = u32x2{0u, 0u};
-            if constexpr (decltype(BIAS)::value) {
-              const int gc = n0 + wn + j * 32 + 8 * g + 4 * h;
-              if (gc < N) bw[g] = *(const u32x2 *)(P.bias + gc);
-            }
+        for (int j = 0; j < 8; ++j) {
+          // bias of this lane's four columns (bf16 words)
+          u32x2 bw{0u, 0u};
+          if constexpr (decltype(BIAS)::value) {
+            const int gc = n0 + wn + j * 16 + 4 * q;
+            if (gc < N) bw = *(const u32x2 *)(P.bias + gc);
           }
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const int row = i * 32 + l;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float x0 = acc[i][j][4 * g] * alpha, x1 = acc[i][j][4 * g + 1] * alpha;
-              float x2 = acc[i][j][4 * g + 2] * alpha, x3 = acc[i][j][4 * g + 3] * alpha;
-              if constexpr (decltype(BIAS)::value) {
-                x0 += __uint_as_float(bw[g].x << 16);
-                x1 += __uint_as_float(bw[g].x & 0xFFFF0000u);
-                x2 += __uint_as_float(bw[g].y << 16);
-                x3 += __uint_as_float(bw[g].y & 0xFFFF0000u);
-              }
-              const u32x2 w{__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2)),
-                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x2, x3}, bf16x2))};
-              const int half = h ^ ((row >> 4) & 1);
-              *(u32x2 *)(wreg + row * RB + chunk_at(row, 4 * j + g) + 8 * half) = w;
+          for (int i = 0; i < 8; ++i) {
+            const int row = i * 16 + r;
+            float x0 = acc4[i][j][0] * alpha, x1 = acc4[i][j][1] * alpha;
+            float x2 = acc4[i][j][2] * alpha, x3 = acc4[i][j][3] * alpha;
+            if constexpr (decltype(BIAS)::value) {
+              x0 += __uint_as_float(bw.x << 16);
+              x1 += __uint_as_float(bw.x & 0xFFFF0000u);
+              x2 += __uint_as_float(bw.y << 16);
+              x3 += __uint_as_float(bw.y & 0xFFFF0000u);
             }
+            const u32x2 w{__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2)),
+                          __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x2, x3}, bf16x2))};
+            *(u32x2 *)(wreg + row * RB + chunk_at(row, 2 * j + (q >> 1)) + 8 * (q & 1)) = w;
           }
         }
       };
@@ -872,10 +894,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         const int idx = (k0 + u) * 64 + el;
         const int row = idx / CPR, ch = idx % CPR;
         vals[u] = *(const u32x4 *)(wreg + row * RB + chunk_at(row, ch));
-        // (with 256 x 256 tiles, the rows of one read share bit 4: row =
-        // 4 (k0 + u) + (lane >> 4), so the half swap is known here)
-        if constexpr (kStag)
-          if (((k0 + u) >> 2) & 1) vals[u] = u32x4{vals[u].z, vals[u].w, vals[u].x, vals[u].y};
         const int gcol = n0 + wn + ch * 8;
         offs[u] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
         if constexpr (AMAX) {
