@@ -491,12 +491,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     } else {
       // Four waves of 128 x 128 (one per SIMD), v_mfma_f32_16x16x128_f8f6f4
       // on C^T: 8 x 8 accumulator blocks of 16 x 16, and a fragment is 16
-      // rows of one operand over a whole K block (lane l: row l & 15, K
-      // bytes 32 (l >> 4) .. +32).  (Per flop it moves half the accumulator
-      // data of the 32 x 32 x 64 instruction; on random codes the chip then
-      // holds a ~8% higher clock.)  A region is one operand of one K block:
-      // region 2 kb + X (X = 0: A, 1: B); consecutive blocks alternate
-      // between the two stages.
+      // rows of one operand over a whole K block.  Lane l holds row l & 15,
+      // 16-byte chunks q and q + 4 of the block (q = l >> 4): A and B take
+      // the same K bytes per lane, so any such split gives the product, and
+      // this one keeps the fragment reads free of LDS bank conflicts
+      // (chunks 2q and 2q + 1 cost an extra cycle per read: ~32k conflict
+      // cycles per tile in SQ_LDS_BANK_CONFLICT).  Per flop the instruction
+      // moves half the accumulator data of the 32 x 32 x 64 one; on random
+      // codes the chip then holds a ~8% higher clock.  A region is one
+      // operand of one K block: region 2 kb + X (X = 0: A, 1: B);
+      // consecutive blocks alternate between the two stages.
       // Step j = 2 s + h runs 32 MFMAs of K block s from registers: A
       // fragments 4h .. 4h + 3 against all eight B fragments (h = 0: A
       // fragment by fragment; h = 1: B fragment by fragment).  Meanwhile it
@@ -526,14 +530,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       auto region = [&](int S, int X) { return smem + X * 2 * OPA + S * OPA; };
       // Byte offset, within a region, of this lane's 16-byte chunk lo (0/1)
       // in fragment 0 of operand X: row r = w + l (w the wave's first row, a
-      // multiple of 16; l = lane & 15), chunk c = 2 (lane >> 4) + lo, at
+      // multiple of 16; l = lane & 15), chunk c = (lane >> 4) + 4 lo, at
       // slot128(r, c); fragment f is 16 rows (2048 bytes) on.
       int rdb[2][2];
 #pragma unroll
       for (int X = 0; X < 2; ++X)
 #pragma unroll
         for (int lo = 0; lo < 2; ++lo) {
-          const int l = kl & 15, c = (kl >> 4) * 2 + lo;
+          const int l = kl & 15, c = (kl >> 4) + 4 * lo;
           rdb[X][lo] = ((X ? wn : wm) + l) * 128 + ((c ^ ((l >> 1) & 7)) << 4);
         }
       auto rd16 = [&](int S, int X, int f) {
