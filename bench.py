@@ -327,6 +327,7 @@ def ceilings(torch, f8lin):
     lib.f8probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p]
     lib.f8probe_mfma_lds.argtypes = lib.f8probe_mfma.argtypes
+    lib.f8probe_mfma_shape.argtypes = [ctypes.c_int] + lib.f8probe_mfma.argtypes
 
     def timed(fn, reps):
         fn()
@@ -429,6 +430,16 @@ def ceilings(torch, f8lin):
     out["mfma_f8_from_registers_random"] = mfma_run(
         lambda: lib.f8probe_mfma(grid, iters, ops.data_ptr(), sink.data_ptr(), clocks.data_ptr(), s.cuda_stream),
         reg_flops, "the same, operands random finite e4m3 codes of either sign")
+    shape_ops = codes(grid * 256 * 128 * 4, "e4m3")
+    sink4 = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    for shape, name, kdepth in ((0, "32x32x64", 64), (1, "16x16x128", 128)):
+        out[f"mfma_f8_{name}_one_wave_per_simd_random"] = mfma_run(
+            lambda: lib.f8probe_mfma_shape(shape, grid, iters, shape_ops.data_ptr(), sink4.data_ptr(),
+                                           clocks.data_ptr(), s.cuda_stream),
+            grid * 4 * iters * 2 * 128 * 128 * kdepth,
+            f"256 workgroups x 4 waves (one per SIMD), 128 x 128 outputs per wave as {name} MFMAs from registers, "
+            "operands random finite e4m3 codes of either sign")
+    del shape_ops, sink4
     lds_iters = iters // 2
     out["mfma_f8_from_lds"] = mfma_run(
         lambda: lib.f8probe_mfma_lds(grid, lds_iters, lds_src.data_ptr(), sink.data_ptr(), clocks.data_ptr(),

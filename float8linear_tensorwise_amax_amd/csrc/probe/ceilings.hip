@@ -18,6 +18,11 @@
 //     from the thread index or random codes loaded once from a buffer: the
 //     matrix cores draw more power when their inputs toggle, and the clock
 //     shows it.
+//   f8probe_mfma_shape: the 256 x 256 tile's MFMA stream from registers, one
+//     wave per SIMD (four per workgroup), 128 x 128 outputs per wave, random
+//     codes: as 16 accumulator blocks of v_mfma_f32_32x32x64_f8f6f4 or as 64
+//     of v_mfma_f32_16x16x128_f8f6f4 -- the two instructions draw different
+//     power per flop, so the clock the chip holds differs.
 //   f8probe_mfma_lds: the GEMM's K loop without its global -> LDS copies: the
 //     same waves and MFMAs, each wave reading its A and B fragments for every
 //     64-byte K step from two 64 KB LDS stages (256 A rows and 256 B rows of
@@ -28,11 +33,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kUnroll = 8;
 
@@ -130,6 +138,59 @@ __global__ __launch_bounds__(512) void mfma_kernel(int iters, const int *__restr
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
   const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
   sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
+// One wave per SIMD, 128 x 128 outputs per wave: SHAPE 0 = 4 x 4 blocks of
+// 32 x 32 x 64, SHAPE 1 = 8 x 8 blocks of 16 x 16 x 128; operands are 128
+// int32 words per thread from ops (thread-major), loaded once.
+template <int SHAPE>
+__global__ __launch_bounds__(256) void mfma_shape_kernel(int iters, const int *__restrict__ ops, float *__restrict__ sink,
+                                                         uint64_t *__restrict__ clocks) {
+  constexpr int NF = SHAPE == 0 ? 4 : 8;  // fragments per operand
+  v8i a[NF], b[NF];
+  const int *p = ops + (int64_t)(blockIdx.x * blockDim.x + threadIdx.x) * 128;
+#pragma unroll
+  for (int i = 0; i < NF; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[i][e] = p[i * 8 + e];
+      b[i][e] = p[64 + i * 8 + e];
+    }
+  typedef typename std::conditional<SHAPE == 0, v16f, v4f>::type acc_t;
+  acc_t acc[NF][NF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = acc_t{};
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        if constexpr (SHAPE == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+      }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NF; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int v = 0; v < (SHAPE == 0 ? 16 : 4); ++v) sum += acc[i][j][v];
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = sum;
   if (threadIdx.x == 0) {
     clocks[2 * blockIdx.x] = t1 - t0;
     clocks[2 * blockIdx.x + 1] = r1 - r0;
@@ -243,6 +304,19 @@ int f8probe_stream(int mode, const void *src, void *dst, int64_t n_bytes, int gr
 int f8probe_mfma(int grid, int iters, const void *ops, float *sink, uint64_t *clocks, void *stream) {
   if (grid < 1 || iters < 1 || !sink || !clocks) return (int)hipErrorInvalidValue;
   mfma_kernel<<<grid, 512, 0, (hipStream_t)stream>>>(iters, (const int *)ops, sink, clocks);
+  return (int)hipGetLastError();
+}
+
+// shape 0 (32 x 32 x 64) or 1 (16 x 16 x 128); grid workgroups of 256 threads;
+// ops: grid * 256 * 128 int32 words of operand codes; sink: grid * 256 floats;
+// clocks as above.  Flops: grid * 4 waves * iters * 2 * 128 * 128 * (64 for
+// shape 0, 128 for shape 1).
+int f8probe_mfma_shape(int shape, int grid, int iters, const void *ops, float *sink, uint64_t *clocks, void *stream) {
+  if (shape < 0 || shape > 1 || grid < 1 || iters < 1 || !ops || !sink || !clocks) return (int)hipErrorInvalidValue;
+  if (shape == 0)
+    mfma_shape_kernel<0><<<grid, 256, 0, (hipStream_t)stream>>>(iters, (const int *)ops, sink, clocks);
+  else
+    mfma_shape_kernel<1><<<grid, 256, 0, (hipStream_t)stream>>>(iters, (const int *)ops, sink, clocks);
   return (int)hipGetLastError();
 }
 
