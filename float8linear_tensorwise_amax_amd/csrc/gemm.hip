@@ -1168,15 +1168,15 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     bool mixed = false;
     for (int i = 1; i < rest.count; ++i)
       mixed |= (rest.p[i].K + kBK - 1) / kBK != (rest.p[0].K + kBK - 1) / kBK;
-    // Big tiles, unless a ragged edge leaves their last round nearly empty.
-    // At equal K a round of small tiles (two per CU) costs ~0.57 of a round of
-    // big ones (4096^3: one big round 55.7 us, two small rounds 64.0 us), so
-    // the small tiles win when 0.6 x their rounds < the big rounds
-    // (12288 x 1600 x 1600: 336 big tiles in two rounds 46.5 us, 1248 small
-    // ones in three 43.0 us; 12288 x 4800 x 1600: four big rounds 99.4 us,
-    // eight small ones 113 us).  A queued batch keeps the big tiles.
+    // Big tiles, unless a ragged edge leaves their last round nearly empty:
+    // the small tiles win when 0.75 x their rounds < the big rounds.  (With
+    // the big tiles on 32 x 32 x 64 MFMAs the factor was 0.6: 12288 x 1600 x
+    // 1600, 336 big tiles in two rounds 46.5 us, 1248 small ones in three
+    // 43.0 us.  On 16 x 16 x 128 MFMAs the big tiles gained ~10% and now take
+    // that shape too: the GPT-1.5B block's N = 1600 forwards, same box, step
+    // 1367-1368 -> 1358-1360 us.)  A queued batch keeps the big tiles.
     const int64_t big_rounds = (big + kCUs - 1) / kCUs, small_rounds = (small + 2 * kCUs - 1) / (2 * kCUs);
-    const bool use_big = big >= kCUs && ((mixed && queue) || 5 * big_rounds <= 3 * small_rounds);
+    const bool use_big = big >= kCUs && ((mixed && queue) || 4 * big_rounds <= 3 * small_rounds);
     // At most one small tile per CU (e.g. 256 tokens: 64 tiles of 128 x 128):
     // tiles of 64 x 128 occupy twice as many CUs (measured: 1024 x 4096 x
     // 4096, 256 small tiles, 25.8 -> 24.1 us; from 384 small tiles on the
