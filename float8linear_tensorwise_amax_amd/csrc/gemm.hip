@@ -172,7 +172,7 @@ constexpr int step_p(int p0, int h0, int k) { return (p0 + ((h0 + k) >> 1)) & 1;
 // into that problem's amax_out with one atomic max when it moves on to
 // another problem or ends.
 template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool PARTIAL, bool DYN = false,
-          bool AMAX = false>
+          bool AMAX = false, bool ODD = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const Batch batch) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
@@ -514,11 +514,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       // wave has then finished the reads of step j - 1 and received all its
       // copies of region j + 2.
       static_assert(TM == 4 && TN == 4 && LA == 8 && LB == 8 && OPA == OPB, "four 128 x 128 wave tiles");
-      // An odd count of K blocks gets a virtual block at the end, so that
-      // the pipeline always runs an even count nkp and one sequence of steps
-      // with no branch: its copies fetch zeros, and its two steps (MFMAs only)
-      // add exact zeros to accumulators that can never hold -0 (same bits).
-      const int virt = nkb & 1, nkp = nkb + virt;
+      // The sequence of steps is fixed by the parity of the count of K
+      // blocks: ODD launches (every problem's count odd) end with a nine-step
+      // tail, the others with a seven-step one.  In the latter an odd count
+      // gets a virtual block at the end, so that one sequence of steps serves
+      // with no branch: its copies fetch zeros, and its two steps (MFMAs
+      // only) add exact zeros to accumulators that can never hold -0 (same
+      // bits).
+      const int virt = ODD ? 0 : nkb & 1, nkp = nkb + virt;
       const int swave = wave;  // (a scalar here)
       // lane-derived addresses are computed per tile from a regenerated lane
       // index (kept across the tile loop they would be spilled, and a spill
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       // steps j .. j + D0 (d = D0 .. 0), the first of parity (P0, H0)
       auto tail = [&](auto D0_, auto P0_, auto H0_, int j) {
         constexpr int D0 = decltype(D0_)::value, p0 = decltype(P0_)::value, h0 = decltype(H0_)::value;
-        static_assert(D0 <= 6, "tail length");
+        static_assert(D0 <= 8, "tail length");
         tstep(int_t<D0>(), int_t<p0>(), int_t<h0>(), j);
         if constexpr (D0 >= 1) tstep(int_t<D0 - 1>(), int_t<step_p(p0, h0, 1)>(), int_t<(h0 + 1) & 1>(), j + 1);
         if constexpr (D0 >= 2) tstep(int_t<D0 - 2>(), int_t<step_p(p0, h0, 2)>(), int_t<(h0 + 2) & 1>(), j + 2);
@@ -679,6 +682,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         if constexpr (D0 >= 4) tstep(int_t<D0 - 4>(), int_t<step_p(p0, h0, 4)>(), int_t<(h0 + 4) & 1>(), j + 4);
         if constexpr (D0 >= 5) tstep(int_t<D0 - 5>(), int_t<step_p(p0, h0, 5)>(), int_t<(h0 + 5) & 1>(), j + 5);
         if constexpr (D0 >= 6) tstep(int_t<D0 - 6>(), int_t<step_p(p0, h0, 6)>(), int_t<(h0 + 6) & 1>(), j + 6);
+        if constexpr (D0 >= 7) tstep(int_t<D0 - 7>(), int_t<step_p(p0, h0, 7)>(), int_t<(h0 + 7) & 1>(), j + 7);
+        if constexpr (D0 >= 8) tstep(int_t<D0 - 8>(), int_t<step_p(p0, h0, 8)>(), int_t<(h0 + 8) & 1>(), j + 8);
       };
 
       // (the host sends only problems of at least four K blocks here)
@@ -700,22 +705,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       __builtin_amdgcn_s_barrier();         // ... and by all
       copy_all(int_t<0>(), int_t<0>(), 2);
       full(int_t<0>(), int_t<0>(), 0);
+      // 2 nkp steps: step 0, rounds of four, and the tail (its first step
+      // always of parity (0, 1))
+      constexpr int kTail = ODD ? 8 : 6;
       int j = 1;
-      if (nkp > 4) {
+      if (nkp > (ODD ? 5 : 4)) {
         // (the loop's first round peeled: the register allocator then keeps
         // the fragments where the loop wants them)
         full(int_t<0>(), int_t<1>(), 1);
         full(int_t<1>(), int_t<0>(), 2);
         full(int_t<1>(), int_t<1>(), 3);
         full(int_t<0>(), int_t<0>(), 4);
-        for (j = 5; j + 4 <= 2 * nkp - 7; j += 4) {
+        for (j = 5; j + 4 <= 2 * nkp - 1 - kTail; j += 4) {
           full(int_t<0>(), int_t<1>(), j);
           full(int_t<1>(), int_t<0>(), j + 1);
           full(int_t<1>(), int_t<1>(), j + 2);
           full(int_t<0>(), int_t<0>(), j + 3);
         }
       }
-      tail(int_t<6>(), int_t<0>(), int_t<1>(), j);
+      tail(int_t<kTail>(), int_t<0>(), int_t<1>(), j);
     }
 
     if constexpr (PARTIAL) {
@@ -1064,10 +1072,26 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 }
 
 // The tiled kernel with or without the output amax (only the forward's and
-// dgrad's format pairs produce a tensor a next layer casts).
+// dgrad's format pairs produce a tensor a next layer casts); four-wave
+// 256 x 256 launches in fixed order whose problems all have an odd count of
+// K blocks take the instantiation with the odd-count tail.
 template <int FA, int FB, int BM, int BN, int WGM, int WGN, int MINB, int G, bool DYN>
 void launch_tiled(const Batch &b, unsigned grid, bool amax, hipStream_t stream) {
   constexpr bool kAmaxPair = FB == 0;
+  constexpr bool kOddTail = BM == 256 && BN == 256 && WGM * WGN == 4 && !DYN;
+  if constexpr (kOddTail) {
+    bool odd = true;
+    for (int i = 0; i < b.count; ++i) odd &= ((b.p[i].K + kBK - 1) / kBK) % 2 == 1;
+    if (odd) {
+      if (kAmaxPair && amax)
+        gemm_fp8_tn_kernel<FA, FB, BM, BN, WGM, WGN, MINB, G, false, DYN, kAmaxPair, true>
+            <<<grid, 64 * WGM * WGN, 0, stream>>>(b);
+      else
+        gemm_fp8_tn_kernel<FA, FB, BM, BN, WGM, WGN, MINB, G, false, DYN, false, true>
+            <<<grid, 64 * WGM * WGN, 0, stream>>>(b);
+      return;
+    }
+  }
   if (kAmaxPair && amax)
     gemm_fp8_tn_kernel<FA, FB, BM, BN, WGM, WGN, MINB, G, false, DYN, kAmaxPair>
         <<<grid, 64 * WGM * WGN, 0, stream>>>(b);
