@@ -808,14 +808,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       static_assert(RB == 256, "staging of the 256 x 256 tiles");
       const int r = el & 15, q = el >> 4;
       auto stage_t = [&](auto BIAS) {
+        // bias of this lane's four columns of each block column j (bf16
+        // words), all eight loads issued before the first use: through a
+        // range-checked buffer, columns at or past N read zeros with no
+        // branch, so the loads share one wait
+        u32x2 bws[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bws[j] = u32x2{0u, 0u};
+        if constexpr (decltype(BIAS)::value) {
+          const __amdgpu_buffer_rsrc_t rbias =
+              __builtin_amdgcn_make_buffer_rsrc((void *)P.bias, (short)0, N * 2, 0x00020000);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            bws[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   rbias, (n0 + wn + j * 16 + 4 * q) * 2, 0, 0));
+          __builtin_amdgcn_sched_barrier(0);  // (kept ahead of the scaling)
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          // bias of this lane's four columns (bf16 words)
-          u32x2 bw{0u, 0u};
-          if constexpr (decltype(BIAS)::value) {
-            const int gc = n0 + wn + j * 16 + 4 * q;
-            if (gc < N) bw = *(const u32x2 *)(P.bias + gc);
-          }
+          const u32x2 bw = bws[j];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int row = i * 16 + r;
@@ -843,13 +854,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
       auto stage_out = [&](auto BIAS) {
         // bias of the kept and the received value of this lane's column pair
         // (cpair, cpair + 1) of each 32-column tile j
+        // (a range-checked buffer: columns at or past N read zeros, no branch)
         float bias_keep[TN], bias_recv[TN];
+        const __amdgpu_buffer_rsrc_t rbias =
+            __builtin_amdgcn_make_buffer_rsrc((void *)P.bias, (short)0, N * 2, 0x00020000);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           bias_keep[j] = bias_recv[j] = 0.0f;
           if constexpr (decltype(BIAS)::value) {
-            const int gc = n0 + wn + j * 32 + (el & 30);
-            const uint32_t bw = gc < N ? *(const uint32_t *)(P.bias + gc) : 0u;
+            const uint32_t bw = __builtin_amdgcn_raw_buffer_load_b32(rbias, (n0 + wn + j * 32 + (el & 30)) * 2, 0, 0);
             const float lo = __uint_as_float(bw << 16), hi = __uint_as_float(bw & 0xFFFF0000u);
             bias_keep[j] = odd ? hi : lo;
             bias_recv[j] = odd ? lo : hi;
