@@ -1234,6 +1234,46 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
     rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
     bool amax = false;
     for (int i = 0; i < rest.count; ++i) amax |= rest.p[i].amax_out != nullptr;
+    // One problem whose last round of big tiles would be less than half full
+    // (12288 x 1600: 336 tiles, a second round of 80): the tile rows of the
+    // full rounds take the big tiles, the rows left over take one round of
+    // small tiles in a launch of their own (measured, same box: 12288 x 1600
+    // x 6400 119.8 -> 116.4 us, 12288 x 1600 x 1600 43.4 -> 42.9 us; two
+    // small tiles on a CU run at about half a big tile's rate, so the gain
+    // is small).
+    if (use_big && rest.count == 1 && !mixed) {
+      const Problem &p = rest.p[0];
+      const int rounds = (tiles + kCUs - 1) / kCUs, last = tiles - (rounds - 1) * kCUs;
+      const int rows_full = (rounds - 1) * kCUs / p.tiles_n * 256;
+      const int small_left = ((p.M - rows_full + 127) / 128) * ((p.N + 127) / 128);
+      if (rounds >= 2 && 2 * last < kCUs && rows_full > 0 && rows_full < p.M && small_left <= 2 * kCUs) {
+        Batch head = rest, left = rest;
+        head.p[0].M = rows_full;
+        head.p[0].tiles_m = rows_full / 256;
+        head.nt_stores = 0;
+        const int head_tiles = head.p[0].tiles_m * head.p[0].tiles_n;
+        if (stag)
+          launch_tiled<FA, FB, 256, 256, 2, 2, 1, 4, false>(head, (unsigned)std::min(head_tiles, kCUs), amax, stream);
+        else
+          launch_tiled<FA, FB, 256, 256, 2, 4, 1, 4, false>(head, (unsigned)std::min(head_tiles, kCUs), amax, stream);
+        Problem &q = left.p[0];
+        q.M = p.M - rows_full;
+        q.a = p.a + (int64_t)rows_full * p.lda;
+        q.c = p.c + (int64_t)rows_full * p.N;
+        left.nt_stores = 0;
+        // (at most one 128 x 128 tile per CU: 64 x 128 tiles, as below)
+        const bool med = small_left <= kCUs;
+        q.tiles_m = (q.M + (med ? 63 : 127)) / (med ? 64 : 128);
+        q.tiles_n = (q.N + 127) / 128;
+        const int left_tiles = q.tiles_m * q.tiles_n;
+        if (med)
+          launch_tiled<FA, FB, 64, 128, 2, 2, 2, 8, false>(left, (unsigned)std::min(left_tiles, 2 * kCUs), amax, stream);
+        else
+          launch_tiled<FA, FB, 128, 128, 2, 2, 2, 8, false>(left, (unsigned)std::min(left_tiles, 2 * kCUs), amax,
+                                                           stream);
+        return;
+      }
+    }
     if (use_big && mixed && queue && fixed_stride_unbalanced(rest, std::min(tiles, kCUs))) {
       std::stable_sort(rest.p, rest.p + rest.count, [](const Problem &x, const Problem &y) { return x.K > y.K; });
       rest.queue = queue;

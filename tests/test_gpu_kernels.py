@@ -226,7 +226,11 @@ def _gemm_gpu(f8, a, fa, b, fb, inv_a, inv_b):
                                  # 64-byte one (its zero half skipped), 13 whole; and 6 blocks with a
                                  # ragged 64-byte one
                                  (4096, 4096, 640), (8192, 4096, 592), (4096, 8192, 576), (4096, 4096, 1664),
-                                 (4096, 4096, 704)])
+                                 (4096, 4096, 704),
+                                 # one problem whose second round of 256x256 tiles would be under half
+                                 # full: the full rounds' rows on 256x256 tiles, the rest in a second
+                                 # launch, on 64x128 tiles (208 ragged rows) or 128x128 ones (3072 rows)
+                                 (9424, 1600, 1600), (12288, 1600, 640)])
 def test_gemm_matches_oracle(f8, fa, fb, mnk):
     M, N, K = mnk
     print(f"gemm fa={fa} fb={fb} M={M} N={N} K={K}", flush=True)
