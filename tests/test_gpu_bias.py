@@ -75,6 +75,19 @@ def test_bias_gpt_qkv_full_size(f8):
     _dbias_check(bf16_to_f64(buf.dbias), bits(dy))
 
 
+def test_bias_with_the_row_split(f8):
+    """9424 x 1600 outputs are 259 tiles of 256 x 256, a second round of
+    three: Y and dX each run as two launches (36 tile rows on 256 x 256
+    tiles, 208 rows on 64 x 128 tiles), both adding the bias to Y."""
+    M, N, K = 9424, 1600, 1600
+    buf, x, w, dy, b = _run(f8, M, N, K, seed=13)
+    ref = oracle.linear_step(bits(x), bits(w), bits(dy), bias_bits=bits(b))
+    gemm_check(bf16_to_f64(buf.y), ref["y"], what="Y + b, row split")
+    gemm_check(bf16_to_f64(buf.dx), ref["dx"], what="dX, row split")
+    gemm_check(bf16_to_f64(buf.dw), ref["dw"], what="dW")
+    _dbias_check(bf16_to_f64(buf.dbias), bits(dy))
+
+
 def test_bias_gradient_is_run_to_run_identical_and_empty_m(f8):
     buf, x, w, dy, b = _run(f8, 4096, 1024, 256, seed=5)
     first = buf.dbias.clone()

@@ -15,6 +15,7 @@ Shapes take every GEMM variant that can write an amax: 256 x 256 tiles,
 128 x 128 tiles with ragged edges and a bias (whose padding rows are not
 stored and must not count), 64 x 128 tiles, the skinny kernel (M <= 64), a
 K-split dX whose amax comes from the reduce kernel, the work-queue backward,
+a lone problem split by rows into two launches that fold into one amax word,
 and a shared-X forward with an amax per output."""
 import numpy as np
 import pytest
@@ -49,7 +50,8 @@ def _same(a, b, what):
     (16, 4096, 4096, 1024, False, True),    # skinny GEMMs
     (256, 1024, 4096, 4096, False, True),   # 64x128 tiles; dX of lin2 split along K (reduce kernel)
     (4096, 4096, 4096, 1024, True, True),   # big tiles with a bias; lin2's dW split, dX alone
-    (4096, 4096, 4096, 1024, False, False)])  # no split scratch: lin2's dX and dW through the work queue
+    (4096, 4096, 4096, 1024, False, False),  # no split scratch: lin2's dX and dW through the work queue
+    (9424, 1600, 1600, 1600, True, True)])   # lin1's Y and lin2's dX in two launches each (row split)
 def test_chain_amax_from_epilogue(f8, M, K1, N1, N2, bias, split):
     print(f"chain M={M} K1={K1} N1={N1} N2={N2} bias={bias} split={split}", flush=True)
     x1 = inputs.random_bf16((M, K1), seed=1).to(DEV)
