@@ -96,6 +96,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
 constexpr int kMinBigK = 4 * kBK;  // shortest K the 256 x 256 tiles take
@@ -909,7 +910,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
     // (in passes of at most 16 chunks per lane, to bound the registers held)
     constexpr int PASS = NCH < 16 ? NCH : 16;
     static_assert(NCH % PASS == 0, "epilogue passes");
-    uint32_t omag = 0;  // AMAX: this lane's max magnitude of the values it stores
+    // AMAX: this lane's max magnitude of the values it stores, per 16-bit
+    // half (both halves of a word compared at once by one packed max)
+    u16x2 omag2 = u16x2{0, 0};
 #pragma unroll
     for (int k0 = 0; k0 < NCH; k0 += PASS) {
       u32x4 vals[PASS];
@@ -922,9 +925,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         const int gcol = n0 + wn + ch * 8;
         offs[u] = gcol < N ? ((wm + row) * N + gcol) * 2 : kOutOfRange;
         if constexpr (AMAX) {
-          // the values this chunk stores (padding rows may hold the bias: they do not count)
-          if (gcol < N && wm + row < rows_c)
-            omag = mag_max2(mag_max2(mag_max2(mag_max2(omag, vals[u].x), vals[u].y), vals[u].z), vals[u].w);
+          // the values this chunk stores (padding rows may hold the bias: they
+          // do not count): a mask, not a branch, drops the others
+          const uint32_t keep = (gcol < N && wm + row < rows_c) ? 0x7FFF7FFFu : 0u;
+          omag2 = __builtin_elementwise_max(omag2, __builtin_bit_cast(u16x2, vals[u].x & keep));
+          omag2 = __builtin_elementwise_max(omag2, __builtin_bit_cast(u16x2, vals[u].y & keep));
+          omag2 = __builtin_elementwise_max(omag2, __builtin_bit_cast(u16x2, vals[u].z & keep));
+          omag2 = __builtin_elementwise_max(omag2, __builtin_bit_cast(u16x2, vals[u].w & keep));
         }
       }
       if (batch.nt_stores) {
@@ -935,7 +942,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_fp8_tn_kernel(const
         for (int u = 0; u < PASS; ++u) __builtin_amdgcn_raw_buffer_store_b128(vals[u], rsc, offs[u], 0, 0);
       }
     }
-    if constexpr (AMAX) red[tid] = max(red[tid], omag);  // after the stores are issued
+    if constexpr (AMAX)  // after the stores are issued
+      red[tid] = max(red[tid], max((uint32_t)omag2.x, (uint32_t)omag2.y));
     __syncthreads();  // staging reads done before the next tile's copies land
     if constexpr (DYN) {
       it = __builtin_amdgcn_readfirstlane(next_item[par]);
