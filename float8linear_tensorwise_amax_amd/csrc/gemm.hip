@@ -28,7 +28,8 @@
 //       small 128 x 128 tile, 4 waves (2 x 2), wave tile 64 x 64, two per CU,
 //             for problems with too few big tiles to fill 256 CUs, or
 //             whose ragged edge would leave the last round of big tiles
-//             nearly empty;
+//             nearly empty, and for the rows a lone problem has left over
+//             after its full rounds of big tiles (a second launch);
 //       medium 64 x 128 tile, 4 waves (2 x 2), wave tile 32 x 64, when even
 //             the small tiles number fewer than the CUs (a few hundred
 //             tokens): twice as many tiles, twice as many busy CUs.
@@ -78,11 +79,13 @@
 //     CU, so that C does not push operand lines out of the caches.
 //   * Epilogue: acc * (inv_a * inv_b) in fp32 (+ the bias in fp32, when the
 //     layer has one: pytorch/ao issue #1297, repro script, whose nn.Linear
-//     layers keep their default bias), then two adjacent columns are
-//     brought into one lane with a DPP swap and rounded to a bf16 pair by
+//     layers keep their default bias; its loads are range-checked buffer
+//     loads issued together), then rounded to bf16 pairs by
 //     v_cvt_pk_bf16_f32 (nearest even; checked against a software rounding on
-//     all 2^32 binary32 patterns), staged through LDS per wave and written as
-//     16-byte row segments.
+//     all 2^32 binary32 patterns): the big tiles' MFMAs run on C^T, so a lane
+//     already holds four adjacent columns, and in the other tiles a DPP swap
+//     brings two adjacent columns into one lane.  The tile is staged through
+//     LDS per wave and written as 16-byte row segments.
 #include <algorithm>
 #include <vector>
 
