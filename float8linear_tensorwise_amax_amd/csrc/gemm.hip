@@ -1239,10 +1239,13 @@ void launch_fmt(Batch &b, float *split_ws, size_t split_bytes, uint32_t *queue, 
       p.splits = 1;
       tiles += p.tiles_m * p.tiles_n;
     }
-    // With several waves of tiles per CU the output would only evict operand
-    // lines from the caches: stream it (measured: -3.5% time at 65536 x 4096 x
-    // 4096, +2% at 4096^3 where each CU writes one tile).
-    rest.nt_stores = tiles >= 4 * (use_big ? kCUs : 2 * kCUs);
+    // With two or more waves of tiles per CU the output would only evict
+    // operand lines from the caches: stream it (measured: -3.5% time at
+    // 65536 x 4096 x 4096, +2% at 4096^3 where each CU writes one tile; from
+    // two rounds instead of four, same box: 12288 x 4800 x 1600 101.8 ->
+    // 99.9 us, 8192 x 4096 x 4096 102.0 -> 100.7 us, the 4096^3 backward
+    // pair 102.9 -> 101.2 us).
+    rest.nt_stores = tiles >= 2 * (use_big ? kCUs : 2 * kCUs);
     bool amax = false;
     for (int i = 0; i < rest.count; ++i) amax |= rest.p[i].amax_out != nullptr;
     // One problem whose last round of big tiles would be less than half full
